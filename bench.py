@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Hybrid-batch attention benchmark (one MI355X).
+
+A step is one pod_attn_hybrid call: one fused launch computing the prefill
+chunk and every decode of the batch.  The same process also times the two
+baselines the pages compare against (paper §3.2): the split launches run
+serially on one stream, and on two streams with an event fork/join.
+
+Default workload: the long-context batch (one 1024-token chunk at offset
+15360 plus 64 decodes at context 16384; 32 query / 8 KV heads, head dim 128,
+bf16, pages of 16 with seeded permuted tables, 1% of K rows scaled by 8).
+Inputs are generated once on the host, uploaded, and resident in HBM before
+timing starts.  Before every timed call the L2s and the Infinity Cache are
+flushed by writing a 1 GiB buffer; each call is timed with HIP events on the
+stream it is launched on.
+
+Prints one JSON line (see the keys below).  --gpus N with N > 1 is refused:
+this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK = 2516.6e12   # dense bf16 MFMA, FLOP/s
+MFMA_F32_PEAK = 157.3e12
+HBM_PEAK = 8.0e12            # bytes/s
+KERNEL_SRC = os.path.join(ROOT, "prefill_decode_hybrid_amd", "csrc", "pod_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def work_counts(b):
+    """Algorithmic work of one hybrid batch (what the method must do)."""
+    hq, hkv, d = b.num_q_heads, b.num_kv_heads, b.head_dim
+    s = 2 if b.spec["dtype"] == "bf16" else 4
+    lens = [] if b.context_lens is None else [int(x) for x in b.context_lens]
+    C, P0 = b.chunk_len, b.chunk_offset
+    f_prefill = 4.0 * d * hq * (C * P0 + C * (C + 1) / 2)
+    f_decode = 4.0 * d * hq * sum(lens)
+    bytes_kv = 2.0 * hkv * d * s * ((C + P0) + sum(lens))
+    bytes_qo = 2.0 * (C + len(lens)) * hq * d * s
+    return dict(f_prefill=f_prefill, f_decode=f_decode, bytes_kv=bytes_kv, bytes_qo=bytes_qo,
+                bytes_total=bytes_kv + bytes_qo)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
+        if fn.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(os.path.dirname(KERNEL_SRC), fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    they are missing or were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_sources") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_mode(fn, steps, flush, torch):
+    ts = []
+    for _ in range(steps):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ts]
+
+
+def cpu_baseline(batch, seconds_target=12.0):
+    """The fp64 oracle on a bounded sample of the same batch, scaled to one batch."""
+    import numpy as np
+    import oracle
+    w = work_counts(batch)
+    lens = batch.context_lens.numpy()
+    rng = np.random.default_rng(0)
+    n_req = min(len(lens), 4)
+    reqs = sorted(rng.choice(len(lens), size=n_req, replace=False).tolist())
+    n_rows = min(batch.chunk_len, 32)
+    rows = sorted(rng.choice(batch.chunk_len, size=n_rows, replace=False).tolist())
+    hq, d = batch.num_q_heads, batch.head_dim
+    C, P0 = batch.chunk_len, batch.chunk_offset
+    f_rows = 4.0 * d * hq * sum(P0 + r + 1 for r in rows)
+    f_reqs = 4.0 * d * hq * sum(int(lens[r]) for r in reqs)
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.prefill(batch.q_prefill, batch.k_pool, batch.v_pool, batch.page_table_prefill, P0,
+                   batch.sm_scale, rows=rows)
+    t1 = time.perf_counter()
+    oracle.decode(batch.q_decode, batch.k_pool, batch.v_pool, batch.page_table_decode,
+                  batch.context_lens, batch.sm_scale, reqs=reqs)
+    t2 = time.perf_counter()
+    # scale each half by its work ratio (visible query-key products)
+    t_batch = (t1 - t0) * (w["f_prefill"] / f_rows) + (t2 - t1) * (w["f_decode"] / f_reqs)
+    try:
+        cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": round(t_batch * 1e6, 1), "unit": "us", "cores": cores, "kind": "oracle",
+            "sample": f"{n_rows} prefill rows x {hq} heads and {n_req} decode requests x {hq} heads of the "
+                      f"same batch, fp64 C+OpenMP, {t2 - t0:.1f} s measured, scaled by visible query-key "
+                      f"products to the whole batch"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload id (1..5); 3 = long context")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-hybrid", action="store_true", help="skip the split-launch baselines")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this hot path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import prefill_decode_hybrid_amd as pod
+    from prefill_decode_hybrid_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pod.load()
+    log(f"[bench] generating config {args.config} (seed {args.seed})")
+    t0 = time.time()
+    batch = inputs.make_batch(args.config, seed=args.seed)
+    log(f"[bench] generated in {time.time() - t0:.1f}s: {inputs.describe(batch)}")
+    dev = batch.to("cuda:0")
+    ctx_host = batch.context_lens.clone().contiguous()
+    att = pod.PodAttention(pod.config_for_batch(batch))
+    op = torch.empty_like(dev.q_prefill)
+    od = torch.empty_like(dev.q_decode)
+    op2 = torch.empty_like(dev.q_prefill)
+    od2 = torch.empty_like(dev.q_decode)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def fused():
+        att.hybrid(dev, op, od, ctx_host)
+
+    def serial():
+        att.prefill_only(dev, op2)
+        att.decode_only(dev, od2, ctx_host)
+
+    def streams():
+        main_s = torch.cuda.current_stream()
+        fork = torch.cuda.Event()
+        fork.record(main_s)
+        s1.wait_event(fork)
+        s2.wait_event(fork)
+        att.prefill_only(dev, op2, stream=s1)
+        att.decode_only(dev, od2, ctx_host, stream=s2)
+        j1, j2 = torch.cuda.Event(), torch.cuda.Event()
+        j1.record(s1)
+        j2.record(s2)
+        main_s.wait_event(j1)
+        main_s.wait_event(j2)
+
+    # untimed check: fusion leaves the result bit-identical to the split launches
+    fused()
+    serial()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(op, op2) and torch.equal(od, od2))
+    finite = bool(torch.isfinite(op.float()).all() and torch.isfinite(od.float()).all())
+    plan = att.stats()
+    log(f"[bench] plan {plan}; fused==split {same}; finite {finite}")
+
+    for _ in range(args.warmup):
+        fused()
+        if not args.only_hybrid:
+            serial()
+            streams()
+    torch.cuda.synchronize()
+
+    host_us = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        fused()
+        host_us.append((time.perf_counter() - a) * 1e6)
+    torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_fused = time_mode(fused, args.steps, flush, torch)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    log(f"[bench] fused median {statistics.median(t_fused) * 1e3:.1f} us")
+    t_serial = t_streams = None
+    if not args.only_hybrid:
+        t_serial = time_mode(serial, args.steps, flush, torch)
+        log(f"[bench] serial median {statistics.median(t_serial) * 1e3:.1f} us")
+        t_streams = time_mode(streams, args.steps, flush, torch)
+        log(f"[bench] two-stream median {statistics.median(t_streams) * 1e3:.1f} us")
+
+    w = work_counts(batch)
+    med = statistics.median(t_fused) * 1e-3  # seconds
+    bf16 = batch.spec["dtype"] == "bf16"
+    mfma_peak = MFMA_BF16_PEAK if bf16 else MFMA_F32_PEAK
+    t_mfma = w["f_prefill"] / mfma_peak
+    t_hbm = w["bytes_total"] / HBM_PEAK
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = w["bytes_total"] / med / 1e9, HBM_PEAK / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = w["f_prefill"] / med / 1e12, mfma_peak / 1e12, "TFLOP/s"
+    workload = f"config{args.config}_{batch.spec['name']}"
+    traffic = load_traffic(workload)
+
+    def q(ts):
+        if not ts:
+            return None
+        s = sorted(ts)
+        return {"median_us": round(statistics.median(s) * 1e3, 2), "p10_us": round(s[len(s) // 10] * 1e3, 2),
+                "p90_us": round(s[(9 * len(s)) // 10] * 1e3, 2)}
+
+    out = {
+        "metric": "hybrid-batch attention us + % of max(MFMA,HBM) roofline; speedup vs split launches",
+        "value": round(med * 1e6, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded; N(0,1) q/k/v, permuted page tables, NaN-poisoned tails)",
+        "config": {"workload": workload, "num_q_heads": batch.num_q_heads, "num_kv_heads": batch.num_kv_heads,
+                   "head_dim": batch.head_dim, "chunk_len": batch.chunk_len, "chunk_offset": batch.chunk_offset,
+                   "num_decode": batch.num_decode, "sum_context": int(batch.context_lens.sum()),
+                   "page_size": 16, "seed": args.seed},
+        "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "overlap_roofline": {"t_roof_us": round(max(t_mfma, t_hbm) * 1e6, 2), "t_mfma_us": round(t_mfma * 1e6, 2),
+                             "t_hbm_us": round(t_hbm * 1e6, 2), "frac": round(max(t_mfma, t_hbm) / med, 4),
+                             "algorithmic_bytes": w["bytes_total"], "prefill_flops": w["f_prefill"],
+                             "decode_flops": w["f_decode"]},
+        "tflops": round((w["f_prefill"] + w["f_decode"]) / med / 1e12, 2),
+        "fused": q(t_fused),
+        "serial": q(t_serial),
+        "two_stream": q(t_streams),
+        "speedup_vs_serial": round(statistics.median(t_serial) / statistics.median(t_fused), 4) if t_serial else None,
+        "speedup_vs_two_stream": round(statistics.median(t_streams) / statistics.median(t_fused), 4) if t_streams else None,
+        "host_call_us": round(statistics.median(host_us), 1),
+        "wall_ms_per_step_incl_flush": round((wall1 - wall0) * 1e3 / args.steps, 4),
+        "fused_equals_split": same,
+        "finite": finite,
+        "plan": plan,
+        "gpu": torch.cuda.get_device_name(0),
+        "kernel_sources": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(batch)
+    print(json.dumps(out), flush=True)
+    att.close()
+
+
+if __name__ == "__main__":
+    main()

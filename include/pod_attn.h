@@ -1,0 +1,183 @@
+/*
+ * pod_attn.h -- C ABI of the hybrid-batch attention library (gfx950).
+ *
+ * One call computes exact softmax attention for a hybrid batch: one causal
+ * chunked-prefill request plus many single-token decode requests over a
+ * paged grouped-query KV cache.  The batch shape is the one POD-Attention is
+ * built for (paper §2.1: a hybrid batch commonly holds one prefill chunk and
+ * several decodes; §3: both sets of inputs reach one attention call), and
+ * the fused entry point computes both halves in a single kernel launch in
+ * which each workgroup picks its role after dispatch from what its compute
+ * unit is already running (paper §4.1, SM-aware CTA scheduling; §4.3, CTA-ID
+ * remapping inside one fused kernel).  The split entry points compute one
+ * half each; run one after the other on one stream or on two streams, they
+ * are the serial and stream-parallel baselines (paper §3.2, FA_Serial and
+ * FA_Streams).
+ *
+ * Math (the result is the plain definition; fusion only changes where and
+ * when tiles run, Silicon & Systems digest, "Virtual CTAs and SM-aware
+ * balance"):
+ *   head h uses kv head g = h / (Hq / Hkv);
+ *   key j of a request sits at pool[page_table[j / page_size]][j % page_size][g][:];
+ *   O = sum_j softmax_j(sm_scale * q . K_j) V_j over the visible keys:
+ *     prefill chunk row i (absolute position chunk_offset + i): j <= chunk_offset + i
+ *     decode request r: j < context_lens[r]
+ *
+ * Layouts (row-major, element type = config dtype for q, k, v and o):
+ *   k_pool, v_pool : [num_pages, page_size, Hkv, head_dim]
+ *   prefill q, o   : [chunk_len, Hq, head_dim]
+ *   decode  q, o   : [num_decode, Hq, head_dim]
+ *   page tables    : int32 physical page ids; the prefill table has at least
+ *                    ceil((chunk_offset + chunk_len) / page_size) entries, the
+ *                    decode table is [num_decode, page_table_stride].
+ * The prefill chunk's own keys (positions chunk_offset .. +chunk_len-1) and
+ * each decode's current token must already be written into the pool.
+ *
+ * Ownership: the caller owns every buffer passed in (all device pointers
+ * except context_lens_host) and the stream.  The handle owns its device
+ * workspace (task queues, merge partials, counters), allocated once by
+ * pod_attn_create from the limits in the config and freed by destroy.
+ *
+ * Asynchrony: every compute call enqueues on `stream` and returns without a
+ * host synchronisation.  Argument validation runs first; when it fails,
+ * nothing is enqueued.  Device page ids outside [0, num_pages) are clamped
+ * to that range (memory-safe, result undefined).  The device context lengths
+ * must equal context_lens_host (the host copy sizes the launch).
+ *
+ * Concurrency: a handle is not thread-safe.  pod_attn_prefill_only and
+ * pod_attn_decode_only use disjoint workspace, so one of each may run at the
+ * same time on two streams; two concurrent calls of the same entry point,
+ * or a hybrid call concurrent with anything else, on one handle race.
+ */
+#ifndef POD_ATTN_H
+#define POD_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream (hipStream_t); NULL is the device's default stream. */
+typedef struct ihipStream_t *pod_stream_t;
+typedef struct pod_attn_handle pod_attn_handle;
+
+enum pod_status {
+    POD_OK = 0,
+    POD_ERR_INVALID_ARG = -1, /* null pointer, length < 1, offset < 0, limit exceeded   */
+    POD_ERR_UNSUPPORTED = -2, /* shape/dtype combination not built (see create)        */
+    POD_ERR_WORKSPACE = -3,   /* the batch needs more workspace than create reserved   */
+    POD_ERR_HIP = -4          /* a HIP runtime call failed; see pod_attn_last_error     */
+};
+
+enum pod_dtype { POD_BF16 = 0, POD_F32 = 1 };
+
+/* Role policy of the fused launch (paper §5.4.2 compares proportional and
+ * 50:50 allocation; §3.3 studies CTA-parallel fusion without SM awareness). */
+enum pod_policy {
+    POD_POLICY_PROPORTIONAL = 0, /* per-CU share of prefill = prefill tasks / all tasks */
+    POD_POLICY_HALF = 1,         /* alternate prefill and decode on every CU          */
+    POD_POLICY_STATIC = 2        /* workgroup id decides the role, no CU awareness     */
+};
+
+typedef struct {
+    int32_t dtype;            /* POD_BF16 or POD_F32                                   */
+    int32_t num_q_heads;      /* Hq                                                    */
+    int32_t num_kv_heads;     /* Hkv; Hq / Hkv must be 1, 2, 4 or 8                    */
+    int32_t head_dim;         /* 64 or 128 (POD_F32: 64 only)                          */
+    int32_t page_size;        /* 16                                                    */
+    float sm_scale;           /* softmax scale; 0 selects 1/sqrt(head_dim)             */
+    int32_t max_chunk_len;    /* largest prefill chunk a call may pass                 */
+    int32_t max_num_decode;   /* largest decode batch                                  */
+    int32_t max_context;      /* largest decode context and largest offset+chunk       */
+    int64_t max_total_context;/* largest sum of decode contexts; 0: max_num_decode*max_context */
+    int32_t wg_per_cu;        /* co-resident workgroups per CU; 0 selects 2 (only 2 built) */
+    int32_t prefill_split_cap_waves; /* cap on prefill tasks, in waves of resident
+                                 workgroups (paper §4.2.3 caps splits at two waves); 0 -> 2 */
+    int32_t policy;           /* enum pod_policy                                       */
+    int32_t device;           /* HIP device ordinal; -1 selects the current device     */
+} pod_attn_config;
+
+typedef struct {
+    const void *q;              /* device [chunk_len, Hq, head_dim]                    */
+    void *o;                    /* device [chunk_len, Hq, head_dim]                    */
+    const int32_t *page_table;  /* device, >= ceil((chunk_offset+chunk_len)/page_size) */
+    int32_t chunk_len;          /* >= 1                                                */
+    int32_t chunk_offset;       /* >= 0: tokens of this request already in the cache  */
+} pod_prefill_args;
+
+typedef struct {
+    const void *q;              /* device [num_decode, Hq, head_dim]                   */
+    void *o;                    /* device [num_decode, Hq, head_dim]                   */
+    const int32_t *page_table;  /* device [num_decode, page_table_stride]              */
+    int32_t page_table_stride;  /* >= ceil(max context / page_size)                    */
+    const int32_t *context_lens;      /* device [num_decode], each >= 1                */
+    const int32_t *context_lens_host; /* host copy of the same values (plans the launch) */
+    int32_t num_decode;         /* >= 1                                                */
+} pod_decode_args;
+
+/* What the last call (or pod_attn_plan) decided; the runtime report the
+ * Silicon & Systems digest asks for ("Isolation and predictability"):
+ * the virtual-workgroup mix, tile choices and the reason for a fallback. */
+typedef struct {
+    int32_t mode;               /* 0 hybrid, 1 prefill only, 2 decode only            */
+    int32_t fallback;           /* 0 none; 1 hybrid without decode ran prefill only;
+                                   2 hybrid without prefill ran decode only            */
+    int32_t num_cus;            /* compute units the plan was made for                 */
+    int32_t wg_per_cu;          /* resident workgroups per CU assumed                  */
+    int32_t grid;               /* workgroups launched                                 */
+    int32_t prefill_rows_per_tile, prefill_heads_per_tile;
+    int32_t prefill_tiles;      /* (row block, kv head, head group) tiles              */
+    int32_t prefill_splits;     /* KV splits per tile                                  */
+    int32_t prefill_split_keys; /* keys per split                                      */
+    int32_t prefill_tasks;      /* tiles * splits (prefill workgroups)                 */
+    int32_t decode_split_tokens;/* tokens per decode wave task                         */
+    int32_t decode_wave_tasks;  /* (request, kv head, token split) units, one wave each */
+    int32_t decode_wg_tasks;    /* decode workgroups (4 wave tasks each)               */
+    int32_t share_num, share_den; /* prefill share of each CU's tickets               */
+    int32_t policy;
+} pod_attn_stats;
+
+/* Validate `cfg`, pick the device, reserve the workspace.  Returns POD_OK and
+ * a handle in *out, or an error and *out = NULL. */
+int pod_attn_create(const pod_attn_config *cfg, pod_attn_handle **out);
+
+/* Free the workspace (synchronises the device first).  NULL is a no-op. */
+int pod_attn_destroy(pod_attn_handle *h);
+
+/* Fused hybrid batch: both halves in one kernel launch.  Either half may be
+ * NULL; the call then runs the other half alone and records why in stats. */
+int pod_attn_hybrid(pod_attn_handle *h, const void *k_pool, const void *v_pool, int64_t num_pages,
+                    const pod_prefill_args *prefill, const pod_decode_args *decode,
+                    pod_stream_t stream);
+
+/* Prefill half only (the compute-bound baseline kernel). */
+int pod_attn_prefill_only(pod_attn_handle *h, const void *k_pool, const void *v_pool,
+                          int64_t num_pages, const pod_prefill_args *prefill, pod_stream_t stream);
+
+/* Decode half only (the bandwidth-bound baseline kernel). */
+int pod_attn_decode_only(pod_attn_handle *h, const void *k_pool, const void *v_pool,
+                         int64_t num_pages, const pod_decode_args *decode, pod_stream_t stream);
+
+/* Copy the plan of the last successful compute call into *out. */
+int pod_attn_get_stats(const pod_attn_handle *h, pod_attn_stats *out);
+
+/* Host-only planning: validate the arguments against `cfg` and fill *out with
+ * the plan a call in `mode` (0 hybrid, 1 prefill only, 2 decode only) would
+ * launch on `num_cus` compute units.  Touches no device; device pointers in
+ * the arguments are only checked for NULL. */
+int pod_attn_plan(const pod_attn_config *cfg, int32_t num_cus, int32_t mode,
+                  const pod_prefill_args *prefill, const pod_decode_args *decode,
+                  pod_attn_stats *out);
+
+/* Static description of a status code. */
+const char *pod_attn_status_string(int status);
+
+/* Text of the last HIP error seen by this handle ("" if none). */
+const char *pod_attn_last_error(const pod_attn_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POD_ATTN_H */

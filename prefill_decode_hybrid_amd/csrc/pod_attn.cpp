@@ -1,0 +1,295 @@
+// C ABI of the hybrid-batch attention library: handle, validation, planning,
+// workspace and launch.  Declarations and contracts are in include/pod_attn.h.
+#include "../../include/pod_attn.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "pod_launch.h"
+#include "pod_plan.h"
+
+struct pod_attn_handle {
+  pod::Shape shape;
+  pod::Limits lim;
+  float sm_scale = 0.0f;
+  int device = 0;
+  char* ws = nullptr;
+  pod::WorkspaceLayout lay;
+  pod_attn_stats stats{};
+  char err[256] = {0};
+};
+
+namespace {
+
+int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, float& scale) {
+  if (!c) return POD_ERR_INVALID_ARG;
+  s.dtype = c->dtype;
+  s.hq = c->num_q_heads;
+  s.hkv = c->num_kv_heads;
+  s.d = c->head_dim;
+  s.page = c->page_size;
+  if (s.hq <= 0 || s.hkv <= 0 || s.d <= 0 || s.page <= 0) return POD_ERR_INVALID_ARG;
+  s.G = s.hq % s.hkv == 0 ? s.hq / s.hkv : 0;
+  int rc = pod::check_shape(s);
+  if (rc) return rc;
+  if (c->max_chunk_len < 1 || c->max_num_decode < 1 || c->max_context < 1 || c->max_total_context < 0)
+    return POD_ERR_INVALID_ARG;
+  if (!(c->sm_scale >= 0.0f) || !std::isfinite(c->sm_scale)) return POD_ERR_INVALID_ARG;
+  if (c->wg_per_cu != 0 && c->wg_per_cu != 2) return POD_ERR_UNSUPPORTED;
+  if (c->prefill_split_cap_waves < 0) return POD_ERR_INVALID_ARG;
+  if (c->policy < pod::kPolicyProportional || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
+  lim.max_chunk_len = c->max_chunk_len;
+  lim.max_num_decode = c->max_num_decode;
+  lim.max_context = c->max_context;
+  lim.max_total_context = c->max_total_context;
+  lim.wg_per_cu = 2;
+  lim.cap_waves = c->prefill_split_cap_waves ? c->prefill_split_cap_waves : 2;
+  lim.policy = c->policy;
+  scale = c->sm_scale > 0.0f ? c->sm_scale : 1.0f / std::sqrt((float)s.d);
+  return POD_OK;
+}
+
+void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
+  std::memset(st, 0, sizeof *st);
+  st->mode = pl.mode;
+  st->fallback = pl.fallback;
+  st->num_cus = pl.num_cus;
+  st->wg_per_cu = pl.wg_per_cu;
+  st->grid = pl.grid;
+  st->prefill_rows_per_tile = pl.rows_per_tile;
+  st->prefill_heads_per_tile = pl.heads_per_tile;
+  st->prefill_tiles = pl.tiles;
+  st->prefill_splits = pl.splits;
+  st->prefill_split_keys = pl.split_keys;
+  st->prefill_tasks = pl.has_p ? pl.p_tasks : 0;
+  st->decode_split_tokens = pl.T;
+  st->decode_wave_tasks = pl.has_d ? pl.d_wave_tasks : 0;
+  st->decode_wg_tasks = pl.has_d ? pl.d_wg_tasks : 0;
+  st->share_num = pl.share_num;
+  st->share_den = pl.share_den;
+  st->policy = pl.policy;
+}
+
+int hip_fail(pod_attn_handle* h, hipError_t e, const char* what) {
+  if (h) std::snprintf(h->err, sizeof h->err, "%s: %s", what, hipGetErrorString(e));
+  return POD_ERR_HIP;
+}
+
+pod::PrefillIn prefill_in(const pod_prefill_args* a) {
+  pod::PrefillIn p;
+  if (a) {
+    p.present = true;
+    p.C = a->chunk_len;
+    p.P0 = a->chunk_offset;
+  }
+  return p;
+}
+
+pod::DecodeIn decode_in(const pod_decode_args* a) {
+  pod::DecodeIn d;
+  if (a) {
+    d.present = true;
+    d.N = a->num_decode;
+    d.stride = a->page_table_stride;
+    d.ctx_host = a->context_lens_host;
+  }
+  return d;
+}
+
+int check_pointers(const pod_prefill_args* p, const pod_decode_args* d) {
+  if (p && (!p->q || !p->o || !p->page_table)) return POD_ERR_INVALID_ARG;
+  if (d && (!d->q || !d->o || !d->page_table || !d->context_lens || !d->context_lens_host))
+    return POD_ERR_INVALID_ARG;
+  return POD_OK;
+}
+
+int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, int64_t num_pages,
+        const pod_prefill_args* pa, const pod_decode_args* da, pod_stream_t stream) {
+  if (!h || !k_pool || !v_pool || num_pages < 1 || num_pages > 0xffffffffLL) return POD_ERR_INVALID_ARG;
+  int rc = check_pointers(pa, da);
+  if (rc) return rc;
+  pod::Plan pl;
+  rc = pod::make_plan(h->shape, h->lim, mode, prefill_in(pa), decode_in(da), &pl);
+  if (rc) return rc;
+
+  const pod::Shape& s = h->shape;
+  pod::PodParams p{};
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.num_pages = (uint32_t)num_pages;
+  p.hq = s.hq;
+  p.hkv = s.hkv;
+  p.scale_log2 = h->sm_scale * 1.4426950408889634f;
+  p.ctrl = reinterpret_cast<uint32_t*>(h->ws + h->lay.ctrl);
+  p.tickets = reinterpret_cast<uint32_t*>(h->ws + h->lay.tickets);
+  p.p_cnt = reinterpret_cast<uint32_t*>(h->ws + h->lay.p_cnt);
+  p.d_cnt = reinterpret_cast<uint32_t*>(h->ws + h->lay.d_cnt);
+  p.p_part = reinterpret_cast<float*>(h->ws + h->lay.p_part);
+  p.d_part = reinterpret_cast<float*>(h->ws + h->lay.d_part);
+  if (pl.has_p) {
+    p.qp = pa->q;
+    p.op = pa->o;
+    p.pt_p = pa->page_table;
+    p.C = pl.C;
+    p.P0 = pl.P0;
+    p.Lp = pl.Lp;
+    p.rows_per_tile = pl.rows_per_tile;
+    p.heads_per_tile = pl.heads_per_tile;
+    p.row_blocks = pl.row_blocks;
+    p.head_groups = pl.head_groups;
+    p.tiles = pl.tiles;
+    p.splits = pl.splits;
+    p.split_keys = pl.split_keys;
+    p.p_tasks = pl.p_tasks;
+  }
+  if (pl.has_d) {
+    p.qd = da->q;
+    p.od = da->o;
+    p.pt_d = da->page_table;
+    p.ctx = da->context_lens;
+    p.stride = da->page_table_stride;
+    p.N = pl.N;
+    p.T = pl.T;
+    p.d_wave_tasks = pl.d_wave_tasks;
+    p.d_wg_tasks = pl.d_wg_tasks;
+  }
+  p.share_num = pl.share_num;
+  p.share_den = pl.share_den;
+  p.policy = pl.policy;
+  p.grid = pl.grid;
+
+  int which = pod::kKernelHybrid;
+  if (!pl.has_d) which = pod::kKernelPrefill;
+  if (!pl.has_p) which = pod::kKernelDecode;
+
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return hip_fail(h, e, "hipSetDevice");
+  if (pl.grid > 0) {
+    e = (hipError_t)pod::launch(which, s.dtype, s.d, s.G, p, pl, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
+  }
+  fill_stats(pl, &h->stats);
+  return POD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pod_attn_create(const pod_attn_config* cfg, pod_attn_handle** out) {
+  if (!out) return POD_ERR_INVALID_ARG;
+  *out = nullptr;
+  pod::Shape s;
+  pod::Limits lim;
+  float scale = 0.0f;
+  int rc = validate_config(cfg, s, lim, scale);
+  if (rc) return rc;
+  if (!pod::have_kernel(s.dtype, s.d, s.G)) return POD_ERR_UNSUPPORTED;
+
+  int dev = cfg->device;
+  hipError_t e;
+  if (dev < 0) {
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return POD_ERR_HIP;
+  }
+  e = hipSetDevice(dev);
+  if (e != hipSuccess) return POD_ERR_HIP;
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus <= 0) return POD_ERR_HIP;
+  lim.num_cus = cus;
+  pod::derive_capacities(s, lim);
+
+  pod_attn_handle* h = new (std::nothrow) pod_attn_handle();
+  if (!h) return POD_ERR_WORKSPACE;
+  h->shape = s;
+  h->lim = lim;
+  h->sm_scale = scale;
+  h->device = dev;
+  h->lay = pod::workspace_layout(s, lim);
+  e = hipMalloc(reinterpret_cast<void**>(&h->ws), h->lay.total);
+  if (e != hipSuccess) {
+    delete h;
+    return POD_ERR_WORKSPACE;
+  }
+  // counters and queue heads start at zero; kernels restore them after each call
+  e = hipMemset(h->ws, 0, h->lay.p_part);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(h->ws);
+    delete h;
+    return POD_ERR_HIP;
+  }
+  *out = h;
+  return POD_OK;
+}
+
+int pod_attn_destroy(pod_attn_handle* h) {
+  if (!h) return POD_OK;
+  int rc = POD_OK;
+  if (hipSetDevice(h->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = POD_ERR_HIP;
+  if (h->ws && hipFree(h->ws) != hipSuccess) rc = POD_ERR_HIP;
+  delete h;
+  return rc;
+}
+
+int pod_attn_hybrid(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,
+                    const pod_prefill_args* prefill, const pod_decode_args* decode, pod_stream_t stream) {
+  return run(h, pod::kModeHybrid, k_pool, v_pool, num_pages, prefill, decode, stream);
+}
+
+int pod_attn_prefill_only(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,
+                          const pod_prefill_args* prefill, pod_stream_t stream) {
+  if (!prefill) return POD_ERR_INVALID_ARG;
+  return run(h, pod::kModePrefill, k_pool, v_pool, num_pages, prefill, nullptr, stream);
+}
+
+int pod_attn_decode_only(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,
+                         const pod_decode_args* decode, pod_stream_t stream) {
+  if (!decode) return POD_ERR_INVALID_ARG;
+  return run(h, pod::kModeDecode, k_pool, v_pool, num_pages, nullptr, decode, stream);
+}
+
+int pod_attn_get_stats(const pod_attn_handle* h, pod_attn_stats* out) {
+  if (!h || !out) return POD_ERR_INVALID_ARG;
+  *out = h->stats;
+  return POD_OK;
+}
+
+int pod_attn_plan(const pod_attn_config* cfg, int32_t num_cus, int32_t mode, const pod_prefill_args* prefill,
+                  const pod_decode_args* decode, pod_attn_stats* out) {
+  if (!out || num_cus < 1 || mode < 0 || mode > 2) return POD_ERR_INVALID_ARG;
+  pod::Shape s;
+  pod::Limits lim;
+  float scale = 0.0f;
+  int rc = validate_config(cfg, s, lim, scale);
+  if (rc) return rc;
+  rc = check_pointers(prefill, decode);
+  if (rc) return rc;
+  lim.num_cus = num_cus;
+  pod::derive_capacities(s, lim);
+  pod::Plan pl;
+  rc = pod::make_plan(s, lim, mode, prefill_in(prefill), decode_in(decode), &pl);
+  if (rc) return rc;
+  fill_stats(pl, out);
+  return POD_OK;
+}
+
+const char* pod_attn_status_string(int status) {
+  switch (status) {
+    case POD_OK: return "ok";
+    case POD_ERR_INVALID_ARG: return "invalid argument";
+    case POD_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case POD_ERR_WORKSPACE: return "workspace too small for this batch";
+    case POD_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* pod_attn_last_error(const pod_attn_handle* h) { return h ? h->err : ""; }
+
+}  // extern "C"

@@ -1,0 +1,943 @@
+// Hybrid-batch attention kernels for gfx950 (CDNA4): prefill tile, split-KV
+// decode, last-arriver merge, and the fused launcher that picks each
+// workgroup's role from the compute unit it landed on.
+//
+// Method (POD-Attention): prefill attention is compute-bound and decode
+// attention bandwidth-bound (paper abstract; §1), so one launch should run
+// both on every compute unit at once (§4).  A regular grid is launched and
+// every workgroup is remapped to a virtual prefill or decode workgroup
+// (§4.3); the choice is made after dispatch from a per-CU ticket, so each CU
+// receives both kinds in a fixed proportion (§4.1 SM-aware CTA scheduling,
+// §5.4.2 proportional allocation).  Decode work is cut into one-wave units
+// (§4.2.3 virtual decode CTAs).  Split partial results are merged by the
+// last split to arrive, so no workgroup ever waits for another (the Silicon
+// & Systems digest: results meet at synchronisation points and the
+// scheduler must not deadlock).
+//
+// The result is exact softmax attention (the digest: fusion changes the
+// order and placement of tiles, not the math); rounding aside, every path
+// computes O = sum_j softmax_j(scale * q.K_j) V_j over the visible keys.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pod_launch.h"
+
+namespace pod {
+
+#define DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+struct Bf16 {
+  static constexpr int bytes = 2;
+};
+struct F32 {
+  static constexpr int bytes = 4;
+};
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ------------------------------------------------------------------ helpers
+DEV float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+DEV float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+// Round-to-nearest-even fp32 pair -> packed bf16 (v_cvt_pk_bf16_f32), a in bits 0..15.
+DEV uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+DEV float safe_max(float m) { return m == kNegInf ? 0.0f : m; }
+
+template <int CTRL>
+DEV float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Sum over each 16-lane row (DPP: swap pairs, swap pair-pairs, half-row mirror, row mirror).
+DEV float row_sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+DEV float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
+DEV int lane_id() { return __lane_id(); }
+DEV int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Key of the compute unit this wave runs on: (XCC, shader engine, array, CU).
+DEV uint32_t cu_key() {
+  uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_REG_HW_ID
+  uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)); // HW_REG_XCC_ID
+  uint32_t cu = (hw >> 8) & 15u, sh = (hw >> 12) & 1u, se = (hw >> 13) & 7u;
+  return ((xcc & 7u) << 8) | (se << 5) | (sh << 4) | cu;
+}
+
+template <int DW>
+DEV void load_dw(uint32_t (&w)[DW], const void* ptr) {
+  static_assert(DW == 2 || DW == 4 || DW == 8, "fragment width");
+  if constexpr (DW == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(ptr);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < DW / 4; ++i) {
+      uint4 v = reinterpret_cast<const uint4*>(ptr)[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  }
+}
+
+template <class E, int DW>
+DEV void to_float(const uint32_t (&w)[DW], float* x) {
+  if constexpr (E::bytes == 2) {
+#pragma unroll
+    for (int i = 0; i < DW; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DW; ++i) x[i] = __uint_as_float(w[i]);
+  }
+}
+
+// Partial dot product of two lane fragments (bf16: v_dot2_f32_bf16, exact products).
+template <class E, int DW>
+DEV float dot_frag(const uint32_t (&a)[DW], const uint32_t (&b)[DW]) {
+  float acc = 0.0f;
+  if constexpr (E::bytes == 2) {
+#pragma unroll
+    for (int i = 0; i < DW; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[i]),
+                                            __builtin_bit_cast(bf16x2_t, b[i]), acc, false);
+  } else {
+#pragma unroll
+    for (int i = 0; i < DW; ++i) acc = fmaf(__uint_as_float(a[i]), __uint_as_float(b[i]), acc);
+  }
+  return acc;
+}
+
+template <class E>
+DEV void store_out(void* base, int64_t idx, float v) {
+  if constexpr (E::bytes == 2) {
+    reinterpret_cast<uint16_t*>(base)[idx] = (uint16_t)(pack_bf16(v, 0.0f) & 0xffffu);
+  } else {
+    reinterpret_cast<float*>(base)[idx] = v;
+  }
+}
+
+// Merge S split partials (acc, m, l) of one output row-head, in split order,
+// and store the normalised row.  part(s) points at split s's [d + 2] block
+// (acc[0..d), m, l) with stride `sstride` floats.  64 lanes cover d.
+template <class E, int D>
+DEV void merge_row(const float* part0, int64_t sstride, int S, void* out, int64_t out_off) {
+  constexpr int EPL = D / 64;
+  const int lane = lane_id();
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, part0[s * sstride + D]);
+  const float Mu = safe_max(M);
+  float acc[EPL] = {};
+  float L = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float* ps = part0 + s * sstride;
+    const float w = fast_exp2(ps[D] - Mu);
+    L += w * ps[D + 1];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += w * ps[lane * EPL + e];
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) store_out<E>(out, out_off + lane * EPL + e, acc[e] * inv);
+}
+
+// Release this wave's stores, count an arrival, report whether it was the last.
+DEV bool arrive_last(uint32_t* counter, uint32_t expected) {
+  uint32_t old = 0;
+  __threadfence();
+  if (lane_id() == 0) old = atomicAdd(counter, 1u);
+  old = __shfl(old, 0, 64);
+  const bool last = (old == expected - 1);
+  if (last) __threadfence();  // acquire the other splits' partials
+  return last;
+}
+
+// ---------------------------------------------------------- decode (a3, a4)
+// One wave computes one (request r, kv head g, token split s) unit for the G
+// query heads of g.  Lane layout: 4 token slots x 16 lanes; lane (slot, j)
+// holds elements [j*D/16, (j+1)*D/16) of the tokens slot, slot+4, slot+8,
+// slot+12 of each 16-token page, so a page is 4 coalesced row loads per
+// operand and a dot product is a 16-lane DPP reduction.  Each slot keeps its
+// own online softmax state; the four are combined at the end.
+template <class E, int D>
+struct DecFrag {
+  static constexpr int EPL = D / 16;
+  static constexpr int DW = EPL * E::bytes / 4;
+};
+
+// Find (request, split, splits) of decode unit `unit` by a wave-wide scan of
+// per-request split counts ceil(L / T) in request order.
+DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S) {
+  const int lane = lane_id();
+  const int maxlen = p.stride * kPageSize;
+  int base = 0;
+  for (int c0 = 0; c0 < p.N; c0 += 64) {
+    const int idx = c0 + lane;
+    int L = idx < p.N ? min(p.ctx[idx], maxlen) : 0;
+    L = max(L, 0);
+    const int cnt = (L + p.T - 1) / p.T;
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (unit < base + total) {
+      const uint64_t hit = __ballot(base + incl > unit);
+      const int first = __builtin_ctzll(hit);
+      r = c0 + first;
+      s = unit - base - (__shfl(incl, first, 64) - __shfl(cnt, first, 64));
+      S = __shfl(cnt, first, 64);
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+template <class E, int D, int G, int PF>
+DEV void decode_wave(const PodParams& p, int wt) {
+  using Fr = DecFrag<E, D>;
+  constexpr int EPL = Fr::EPL, DW = Fr::DW;
+  const int lane = lane_id();
+  const int hkv = p.hkv;
+  const int g = wt % hkv;
+  const int unit = wt / hkv;
+  int r, s, S;
+  if (!locate_unit(p, unit, r, s, S)) return;
+  r = __builtin_amdgcn_readfirstlane(r);
+  s = __builtin_amdgcn_readfirstlane(s);
+  S = __builtin_amdgcn_readfirstlane(S);
+  const int L = min(p.ctx[r], p.stride * kPageSize);
+  const int t0 = s * p.T;
+  const int t1 = min(t0 + p.T, L);
+  const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
+  const int slot = lane >> 4, j = lane & 15;
+
+  int pid = 0;
+  if (lane < npg) pid = p.pt_d[(int64_t)r * p.stride + t0 / kPageSize + lane];
+  pid = (int)min((uint32_t)pid, p.num_pages - 1u);
+
+  uint32_t q[G][DW];
+  {
+    const char* qb = reinterpret_cast<const char*>(p.qd) +
+                     (((int64_t)r * p.hq + (int64_t)g * G) * D + j * EPL) * E::bytes;
+#pragma unroll
+    for (int h = 0; h < G; ++h) load_dw<DW>(q[h], qb + (int64_t)h * D * E::bytes);
+  }
+  const int64_t tok_bytes = (int64_t)hkv * D * E::bytes;
+  const int64_t page_bytes = kPageSize * tok_bytes;
+  const int64_t lane_off = ((int64_t)g * D + j * EPL) * E::bytes + slot * tok_bytes;
+  const char* kb = reinterpret_cast<const char*>(p.k_pool) + lane_off;
+  const char* vb = reinterpret_cast<const char*>(p.v_pool) + lane_off;
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegInf;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+  }
+
+  constexpr int NB = PF + 1;
+  uint32_t kr[NB][4][DW], vr[NB][4][DW];
+
+  auto issue = [&](uint32_t (&kd)[4][DW], uint32_t (&vd)[4][DW], int i) {
+    const int64_t page = __builtin_amdgcn_readlane(pid, i);
+    const int64_t off = page * page_bytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_dw<DW>(kd[u], kb + off + 4 * u * tok_bytes);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_dw<DW>(vd[u], vb + off + 4 * u * tok_bytes);
+  };
+
+  auto consume = [&](const uint32_t (&kd)[4][DW], const uint32_t (&vd)[4][DW], int i) {
+    const int tb = t0 + i * kPageSize + slot;
+    float sc[4][G];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[u][h] = row_sum16(dot_frag<E, DW>(q[h], kd[u]));
+    bool valid[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) valid[u] = (tb + 4 * u) < t1;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sc[u][h] = valid[u] ? sc[u][h] * p.scale_log2 : kNegInf;
+        mx = fmaxf(mx, sc[u][h]);
+      }
+      const float mnew = fmaxf(m[h], mx);
+      const float mu = safe_max(mnew);
+      const float alpha = fast_exp2(m[h] - mu);
+      float ps = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sc[u][h] = fast_exp2(sc[u][h] - mu);
+        ps += sc[u][h];
+      }
+      l[h] = l[h] * alpha + ps;
+      m[h] = mnew;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float v[EPL];
+      to_float<E, DW>(vd[u], v);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[e] = valid[u] ? v[e] : 0.0f;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(sc[u][h], v[e], acc[h][e]);
+    }
+  };
+
+#pragma unroll
+  for (int b = 0; b < PF; ++b)
+    if (b < npg) issue(kr[b], vr[b], b);
+  for (int i0 = 0; i0 < npg; i0 += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int i = i0 + b;
+      if (i < npg) {
+        if (i + PF < npg) issue(kr[(b + PF) % NB], vr[(b + PF) % NB], i + PF);
+        consume(kr[b], vr[b], i);
+      }
+    }
+  }
+
+  // combine the four slots: common max, rescale, sum across rows of 16 lanes
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = fmaxf(m[h], xor_lane(m[h], 16));
+    M = fmaxf(M, xor_lane(M, 32));
+    const float f = fast_exp2(m[h] - safe_max(M));
+    l[h] *= f;
+    l[h] += xor_lane(l[h], 16);
+    l[h] += xor_lane(l[h], 32);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float a = acc[h][e] * f;
+      a += xor_lane(a, 16);
+      a += xor_lane(a, 32);
+      acc[h][e] = a;
+    }
+    m[h] = M;
+  }
+
+  if (S == 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if ((h & 3) == slot) {
+        const float inv = 1.0f / l[h];
+        const int64_t o = ((int64_t)r * p.hq + (int64_t)g * G + h) * D + j * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) store_out<E>(p.od, o + e, acc[h][e] * inv);
+      }
+    }
+    return;
+  }
+
+  // partial of this split: [G][D] acc, [G] m, [G] l
+  float* part = p.d_part + (int64_t)wt * G * (D + 2);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if ((h & 3) == slot) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part[h * D + j * EPL + e] = acc[h][e];
+      if (j == 0) {
+        part[G * D + h] = m[h];
+        part[G * D + G + h] = l[h];
+      }
+    }
+  }
+  uint32_t* cnt = p.d_cnt + (int64_t)r * hkv + g;
+  if (!arrive_last(cnt, (uint32_t)S)) return;
+
+  // last split merges all S partials of (r, g) in split order
+  const int unit0 = unit - s;
+  constexpr int MPL = D / 64;
+  for (int h = 0; h < G; ++h) {
+    float M = kNegInf;
+    for (int ss = 0; ss < S; ++ss) {
+      const float* ps = p.d_part + ((int64_t)(unit0 + ss) * hkv + g) * G * (D + 2);
+      M = fmaxf(M, ps[G * D + h]);
+    }
+    const float Mu = safe_max(M);
+    float a[MPL] = {};
+    float Lsum = 0.0f;
+    for (int ss = 0; ss < S; ++ss) {
+      const float* ps = p.d_part + ((int64_t)(unit0 + ss) * hkv + g) * G * (D + 2);
+      const float w = fast_exp2(ps[G * D + h] - Mu);
+      Lsum += w * ps[G * D + G + h];
+#pragma unroll
+      for (int e = 0; e < MPL; ++e) a[e] += w * ps[h * D + lane * MPL + e];
+    }
+    const float inv = 1.0f / Lsum;
+    const int64_t o = ((int64_t)r * p.hq + (int64_t)g * G + h) * D + lane * MPL;
+#pragma unroll
+    for (int e = 0; e < MPL; ++e) store_out<E>(p.od, o + e, a[e] * inv);
+  }
+  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class E, int D, int G, int PF>
+DEV void decode_wg(const PodParams& p, int wg_task) {
+  const int wt = wg_task * kWavesPerWG + wave_id();
+  if (wt < p.d_wave_tasks) decode_wave<E, D, G, PF>(p, wt);
+}
+
+// ---------------------------------------------------------- prefill (a2, a4)
+// A prefill task is (tile, KV split).  A tile is (row block, kv head g, head
+// group): 4 waves, wave w takes 32 (bf16) or 64 (fp32) consecutive chunk
+// rows of one query head of g.  K/V blocks of the split's key range are
+// staged once in LDS and shared by the 4 waves (the GQA heads of one kv
+// head reuse the same keys).
+struct TaskGeom {
+  int tile, split, rb, g, hg;
+  int head, row0;     // this wave's head and first row
+  int k0, k1;         // split key range, clipped to the tile's causal end
+  int kw;             // this wave's last visible key + 1 within the split
+};
+
+template <int RPW>
+DEV TaskGeom prefill_geom(const PodParams& p, int task) {
+  TaskGeom t;
+  int i = task;
+  t.g = i % p.hkv;
+  i /= p.hkv;
+  t.hg = i % p.head_groups;
+  i /= p.head_groups;
+  const int rbi = i % p.row_blocks;
+  t.split = i / p.row_blocks;
+  t.rb = p.row_blocks - 1 - rbi;  // longest (latest) row blocks first
+  t.tile = (t.rb * p.head_groups + t.hg) * p.hkv + t.g;
+  const int w = wave_id();
+  const int G = p.hq / p.hkv;
+  t.head = t.g * G + t.hg * p.heads_per_tile + (w % p.heads_per_tile);
+  t.row0 = t.rb * p.rows_per_tile + (w / p.heads_per_tile) * RPW;
+  const int tile_end = p.P0 + min(p.C, (t.rb + 1) * p.rows_per_tile);  // causal end of the tile
+  t.k0 = t.split * p.split_keys;
+  t.k1 = min(t.k0 + p.split_keys, tile_end);
+  t.kw = min(t.k1, p.P0 + min(p.C, t.row0 + RPW));
+  return t;
+}
+
+// bf16 prefill tile: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16.
+// Lane l owns query row (l & 31) of its wave; its half h = l >> 5 owns half of
+// every 32-key score column, so row max and row sum are mostly in-lane.
+template <int D>
+struct PfBf16 {
+  static constexpr int RPW = 32;
+  static constexpr int BN = 64;                       // keys per staged block
+  static constexpr int KSTR = (D + 8) * 2;            // K row stride (bytes), padded
+  static constexpr int VSTR = (BN + 8) * 2;           // V^T row stride (bytes), padded
+  static constexpr int KBYTES = BN * KSTR;
+  static constexpr int STAGE = KBYTES + D * VSTR;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int CH = D / 8;                    // 16-byte chunks per key row
+  static constexpr int KLOADS = CH / 4;               // K chunks per thread per block
+};
+
+// Position of key k (0..63) inside a V^T row: bits 2 and 3 swapped, so that
+// the 8 keys one MFMA lane feeds for P^T are contiguous (see prefill_tile).
+DEV int vt_pos(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
+
+template <int D>
+DEV void stage_load_bf16(const PodParams& p, int kb0, uint4 (&kreg)[PfBf16<D>::KLOADS], uint4 (&vreg)[4]) {
+  using C = PfBf16<D>;
+  const int tid = threadIdx.x;
+  const int64_t tok_bytes = (int64_t)p.hkv * D * 2;
+#pragma unroll
+  for (int i = 0; i < C::KLOADS; ++i) {
+    const int idx = tid + 256 * i;
+    const int key = kb0 + idx / C::CH;
+    const int c = idx % C::CH;
+    kreg[i] = make_uint4(0, 0, 0, 0);
+    if (key < p.Lp) {
+      const int64_t page = min((uint32_t)p.pt_p[key >> 4], p.num_pages - 1u);
+      const char* src = reinterpret_cast<const char*>(p.k_pool) + (page * kPageSize + (key & 15)) * tok_bytes + c * 16;
+      kreg[i] = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+  if (tid < 16 * C::CH) {
+    const int c = tid >> 4, kq = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb0 + 4 * kq + i;
+      vreg[i] = make_uint4(0, 0, 0, 0);
+      if (key < p.Lp) {
+        const int64_t page = min((uint32_t)p.pt_p[key >> 4], p.num_pages - 1u);
+        const char* src = reinterpret_cast<const char*>(p.v_pool) + (page * kPageSize + (key & 15)) * tok_bytes + c * 16;
+        vreg[i] = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+  }
+}
+
+template <int D>
+DEV void stage_store_bf16(char* st, const uint4 (&kreg)[PfBf16<D>::KLOADS], const uint4 (&vreg)[4]) {
+  using C = PfBf16<D>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::KLOADS; ++i) {
+    const int idx = tid + 256 * i;
+    *reinterpret_cast<uint4*>(st + (idx / C::CH) * C::KSTR + (idx % C::CH) * 16) = kreg[i];
+  }
+  if (tid < 16 * C::CH) {
+    const int c = tid >> 4, kq = tid & 15;
+    char* vt = st + C::KBYTES + vt_pos(4 * kq) * 2;
+    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
+    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
+    const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
+    const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      uint2 w;
+      w.x = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
+      w.y = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
+      *reinterpret_cast<uint2*>(vt + (8 * c + e) * C::VSTR) = w;
+    }
+  }
+}
+
+// Tile-level arrival and merge, shared by both prefill flavours.
+template <class E, int D, int RPW>
+DEV void prefill_finish_split(const PodParams& p, const TaskGeom& t, int task, int* flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t old = atomicAdd(p.p_cnt + t.tile, 1u);
+    *flag = (old == (uint32_t)p.splits - 1u);
+  }
+  __syncthreads();
+  if (!*flag) return;
+  __threadfence();
+  const int w = wave_id();
+  const int64_t rowheads = (int64_t)RPW * kWavesPerWG;
+  // Tasks of one tile differ only in their split: task = split * tiles + (tile
+  // position), so split s of this tile is task - (split - s) * tiles.
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int row = t.row0 + rr;
+    if (row >= p.C) break;
+    const int64_t first = ((int64_t)(task - t.split * p.tiles) * rowheads + w * RPW + rr) * (D + 2);
+    const int64_t sstride = (int64_t)p.tiles * rowheads * (D + 2);
+    merge_row<E, D>(p.p_part + first, sstride, p.splits, p.op, ((int64_t)row * p.hq + t.head) * D);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(p.p_cnt + t.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+DEV void prefill_tile_bf16(const PodParams& p, int task, char* smem, int* flag) {
+  using C = PfBf16<D>;
+  constexpr int KS = D / 16;   // MFMA k-steps over d
+  constexpr int DB = D / 32;   // 32-wide d blocks of O^T
+  const TaskGeom t = prefill_geom<C::RPW>(p, task);
+  const int lane = lane_id();
+  const int half = lane >> 5, rl = lane & 31;
+  const int row = t.row0 + rl;
+
+  // kv-head offset folded into the pool pointers
+  PodParams pk = p;
+  pk.k_pool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)t.g * D * 2;
+  pk.v_pool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)t.g * D * 2;
+
+  // Q^T operand: lane holds d = 16 ks + 8 half .. +8 of its row
+  bf16x8_t qf[KS];
+  {
+    const char* qrow = reinterpret_cast<const char*>(p.qp) + (((int64_t)row * p.hq + t.head) * D + 8 * half) * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < p.C) v = *reinterpret_cast<const uint4*>(qrow + ks * 32);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = 0.0f;
+  float m = kNegInf, l = 0.0f;
+
+  const int nblk = t.k1 > t.k0 ? (t.k1 - t.k0 + C::BN - 1) / C::BN : 0;
+  const int lim = p.P0 + row;  // last visible key of this lane's row
+
+  uint4 kreg[C::KLOADS], vreg[4];
+  if (nblk > 0) {
+    stage_load_bf16<D>(pk, t.k0, kreg, vreg);
+    stage_store_bf16<D>(smem, kreg, vreg);
+  }
+  __syncthreads();
+  for (int b = 0; b < nblk; ++b) {
+    const int kb0 = t.k0 + b * C::BN;
+    char* st = smem + (b & 1) * C::STAGE;
+    if (b + 1 < nblk) stage_load_bf16<D>(pk, kb0 + C::BN, kreg, vreg);
+    if (kb0 < t.kw) {
+      // ---- scores S^T (keys x rows), two 32-key tiles
+      f32x16_t sc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[tt][j] = 0.0f;
+        const char* kr = st + (32 * tt + rl) * C::KSTR + 16 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
+          sc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[tt], 0, 0, 0);
+        }
+      }
+      // ---- scale, causal mask, online softmax (base 2)
+      const bool need_mask = (kb0 + C::BN - 1) > (p.P0 + t.row0);
+      float mx = kNegInf;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float s = sc[tt][j] * p.scale_log2;
+          if (need_mask) {
+            const int key = kb0 + 32 * tt + 8 * (j >> 2) + 4 * half + (j & 3);
+            s = key <= lim ? s : kNegInf;
+          }
+          sc[tt][j] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, xor_lane(mx, 32));
+      const float mnew = fmaxf(m, mx);
+      const float mu = safe_max(mnew);
+      const float alpha = fast_exp2(m - mu);
+      float ps = 0.0f;
+      bf16x8_t pf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const float e0 = fast_exp2(sc[ks >> 1][8 * (ks & 1) + 2 * q2] - mu);
+          const float e1 = fast_exp2(sc[ks >> 1][8 * (ks & 1) + 2 * q2 + 1] - mu);
+          ps += e0 + e1;
+          w4[q2] = pack_bf16(e0, e1);
+        }
+        pf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+      }
+      l = l * alpha + ps;
+      m = mnew;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+      }
+      // ---- O^T += V^T P^T
+      const char* vt = st + C::KBYTES;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char* vr = vt + (32 * db + rl) * C::VSTR + 16 * half;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vr + ks * 32);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
+        }
+      }
+    }
+    if (b + 1 < nblk) stage_store_bf16<D>(smem + ((b + 1) & 1) * C::STAGE, kreg, vreg);
+    __syncthreads();
+  }
+
+  const float ltot = l + xor_lane(l, 32);
+  if (p.splits == 1) {
+    if (row < p.C) {
+      const float inv = 1.0f / ltot;
+      char* orow = reinterpret_cast<char*>(p.op) + ((int64_t)row * p.hq + t.head) * D * 2;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          uint2 w;
+          w.x = pack_bf16(o[db][4 * jq] * inv, o[db][4 * jq + 1] * inv);
+          w.y = pack_bf16(o[db][4 * jq + 2] * inv, o[db][4 * jq + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + (32 * db + 8 * jq + 4 * half) * 2) = w;
+        }
+    }
+    return;
+  }
+  // split partial: unnormalised acc, m (base 2), l
+  const int64_t rowheads = (int64_t)C::RPW * kWavesPerWG;
+  float* pr = p.p_part + ((int64_t)task * rowheads + wave_id() * C::RPW + rl) * (D + 2);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq)
+      *reinterpret_cast<float4*>(pr + 32 * db + 8 * jq + 4 * half) =
+          make_float4(o[db][4 * jq], o[db][4 * jq + 1], o[db][4 * jq + 2], o[db][4 * jq + 3]);
+  if (half == 0) {
+    pr[D] = m;
+    pr[D + 1] = ltot;
+  }
+  prefill_finish_split<Bf16, D, C::RPW>(p, t, task, flag);
+}
+
+// fp32 prefill tile (exact fp32, VALU): lane = one query row, K/V blocks of 32
+// keys in LDS read as broadcasts.
+template <int D>
+struct PfF32 {
+  static constexpr int RPW = 64;
+  static constexpr int BN = 32;
+  static constexpr int LDS = 2 * BN * D * 4;
+};
+
+template <int D>
+DEV void prefill_tile_f32(const PodParams& p, int task, char* smem, int* flag) {
+  using C = PfF32<D>;
+  const TaskGeom t = prefill_geom<C::RPW>(p, task);
+  const int lane = lane_id();
+  const int row = t.row0 + lane;
+  float* ks = reinterpret_cast<float*>(smem);
+  float* vs = ks + C::BN * D;
+
+  float q[D], acc[D];
+  {
+    const float* qrow = reinterpret_cast<const float*>(p.qp) + ((int64_t)row * p.hq + t.head) * D;
+#pragma unroll
+    for (int e = 0; e < D; e += 4) {
+      float4 v = make_float4(0, 0, 0, 0);
+      if (row < p.C) v = *reinterpret_cast<const float4*>(qrow + e);
+      q[e] = v.x;
+      q[e + 1] = v.y;
+      q[e + 2] = v.z;
+      q[e + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.0f;
+  float m = kNegInf, l = 0.0f;
+  const int lim = p.P0 + row;
+  const int nblk = t.k1 > t.k0 ? (t.k1 - t.k0 + C::BN - 1) / C::BN : 0;
+  const int64_t tok = (int64_t)p.hkv * D;
+  const float* kpool = reinterpret_cast<const float*>(p.k_pool) + (int64_t)t.g * D;
+  const float* vpool = reinterpret_cast<const float*>(p.v_pool) + (int64_t)t.g * D;
+  constexpr int V4 = C::BN * D / 4;  // float4 chunks per operand block
+  for (int b = 0; b < nblk; ++b) {
+    const int kb0 = t.k0 + b * C::BN;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < V4; idx += 256) {
+      const int kk = idx / (D / 4), c = idx % (D / 4);
+      const int key = kb0 + kk;
+      float4 kv = make_float4(0, 0, 0, 0), vv = kv;
+      if (key < p.Lp) {
+        const int64_t page = min((uint32_t)p.pt_p[key >> 4], p.num_pages - 1u);
+        const int64_t off = (page * kPageSize + (key & 15)) * tok + 4 * c;
+        kv = *reinterpret_cast<const float4*>(kpool + off);
+        vv = *reinterpret_cast<const float4*>(vpool + off);
+      }
+      reinterpret_cast<float4*>(ks)[idx] = kv;
+      reinterpret_cast<float4*>(vs)[idx] = vv;
+    }
+    __syncthreads();
+    if (kb0 >= t.kw) continue;
+    float s[C::BN];
+    float mx = kNegInf;
+#pragma unroll
+    for (int kk = 0; kk < C::BN; ++kk) {
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) a = fmaf(q[e], ks[kk * D + e], a);
+      a *= p.scale_log2;
+      a = (kb0 + kk <= lim) ? a : kNegInf;
+      s[kk] = a;
+      mx = fmaxf(mx, a);
+    }
+    const float mnew = fmaxf(m, mx);
+    const float mu = safe_max(mnew);
+    const float alpha = fast_exp2(m - mu);
+    float ps = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < C::BN; ++kk) {
+      s[kk] = fast_exp2(s[kk] - mu);
+      ps += s[kk];
+    }
+    l = l * alpha + ps;
+    m = mnew;
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      float a = acc[e] * alpha;
+#pragma unroll
+      for (int kk = 0; kk < C::BN; ++kk) a = fmaf(s[kk], vs[kk * D + e], a);
+      acc[e] = a;
+    }
+  }
+  if (p.splits == 1) {
+    if (row < p.C) {
+      const float inv = 1.0f / l;
+      float* orow = reinterpret_cast<float*>(p.op) + ((int64_t)row * p.hq + t.head) * D;
+#pragma unroll
+      for (int e = 0; e < D; e += 4)
+        *reinterpret_cast<float4*>(orow + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+    }
+    return;
+  }
+  const int64_t rowheads = (int64_t)C::RPW * kWavesPerWG;
+  float* pr = p.p_part + ((int64_t)task * rowheads + wave_id() * C::RPW + lane) * (D + 2);
+#pragma unroll
+  for (int e = 0; e < D; e += 4) *reinterpret_cast<float4*>(pr + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  pr[D] = m;
+  pr[D + 1] = l;
+  prefill_finish_split<F32, D, C::RPW>(p, t, task, flag);
+}
+
+template <class E, int D>
+struct PfSel;
+template <int D>
+struct PfSel<Bf16, D> {
+  static constexpr int LDS = PfBf16<D>::LDS;
+  static DEV void run(const PodParams& p, int task, char* smem, int* flag) { prefill_tile_bf16<D>(p, task, smem, flag); }
+};
+template <int D>
+struct PfSel<F32, D> {
+  static constexpr int LDS = PfF32<D>::LDS;
+  static DEV void run(const PodParams& p, int task, char* smem, int* flag) { prefill_tile_f32<D>(p, task, smem, flag); }
+};
+
+// ------------------------------------------------------------------ kernels
+// Pages in flight per decode wave: the fused kernel keeps 2 WGs per CU, so its
+// decode waves prefetch deeper; the decode-only kernel runs more waves instead.
+template <int G>
+constexpr int fused_pf() { return G >= 8 ? 1 : 2; }
+constexpr int kDecodePF = 1;
+template <int G>
+constexpr int decode_min_blocks() { return G >= 4 ? 2 : 4; }  // VGPR budget 256 / 128
+
+template <class E, int D, int G>
+__global__ __launch_bounds__(256, 2) void pod_prefill_kernel(PodParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[PfSel<E, D>::LDS];
+  __shared__ int flag;
+  PfSel<E, D>::run(p, blockIdx.x, smem, &flag);
+}
+
+template <class E, int D, int G>
+__global__ __launch_bounds__(256, decode_min_blocks<G>()) void pod_decode_kernel(PodParams p) {
+  decode_wg<E, D, G, kDecodePF>(p, blockIdx.x);
+}
+
+// Fused hybrid kernel.  Each workgroup takes a ticket on its CU's counter;
+// the ticket's position in a period of share_den decides the role so that
+// share_num of every share_den workgroups arriving on a CU run prefill,
+// prefill first (paper §4.1 and §5.4.2).  The task is then claimed from that
+// role's queue, or from the other queue once the first is exhausted; since
+// the grid equals the task count, every claim succeeds and every task runs
+// exactly once, with no workgroup ever waiting for another.
+template <class E, int D, int G>
+__global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[PfSel<E, D>::LDS];
+  __shared__ int role_task[2];
+  __shared__ int flag;
+  if (threadIdx.x == 0) {
+    int role, task;
+    if (p.policy == kPolicyStatic) {
+      role = (int)blockIdx.x < p.p_tasks ? 0 : 1;
+      task = role == 0 ? (int)blockIdx.x : (int)blockIdx.x - p.p_tasks;
+    } else {
+      const uint32_t t = atomicAdd(p.tickets + cu_key(), 1u) % (uint32_t)p.share_den;
+      const uint32_t num = (uint32_t)p.share_num, den = (uint32_t)p.share_den;
+      const bool pre = ((t + 1) * num + den - 1) / den > (t * num + den - 1) / den;
+      role = pre ? 0 : 1;
+      uint32_t x = atomicAdd(p.ctrl + role, 1u);
+      const uint32_t lim = role == 0 ? (uint32_t)p.p_tasks : (uint32_t)p.d_wg_tasks;
+      if (x >= lim) {
+        role ^= 1;
+        x = atomicAdd(p.ctrl + role, 1u);
+      }
+      task = (int)x;
+      const uint32_t done = __hip_atomic_fetch_add(p.ctrl + 2, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == (uint32_t)p.grid - 1u) {  // every workgroup has claimed: reset the queues
+        __hip_atomic_store(p.ctrl + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctrl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctrl + 2, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    role_task[0] = role;
+    role_task[1] = task;
+  }
+  __syncthreads();
+  const int role = role_task[0], task = role_task[1];
+  if (role == 0) {
+    if (task < p.p_tasks) PfSel<E, D>::run(p, task, smem, &flag);
+  } else {
+    if (task < p.d_wg_tasks) decode_wg<E, D, G, fused_pf<G>()>(p, task);
+  }
+}
+
+// ------------------------------------------------------------------- launch
+template <class E, int D, int G>
+static int launch_t(int which, const PodParams& p, const Plan& pl, hipStream_t s) {
+  const dim3 block(256);
+  switch (which) {
+    case kKernelHybrid:
+      hipLaunchKernelGGL((pod_hybrid_kernel<E, D, G>), dim3(pl.grid), block, 0, s, p);
+      break;
+    case kKernelPrefill:
+      hipLaunchKernelGGL((pod_prefill_kernel<E, D, G>), dim3(pl.p_tasks), block, 0, s, p);
+      break;
+    default:
+      hipLaunchKernelGGL((pod_decode_kernel<E, D, G>), dim3(pl.d_wg_tasks), block, 0, s, p);
+      break;
+  }
+  return (int)hipGetLastError();
+}
+
+#define POD_KERNEL_LIST(X)  \
+  X(kBf16, Bf16, 128, 1)    \
+  X(kBf16, Bf16, 128, 2)    \
+  X(kBf16, Bf16, 128, 4)    \
+  X(kBf16, Bf16, 128, 8)    \
+  X(kBf16, Bf16, 64, 1)     \
+  X(kBf16, Bf16, 64, 2)     \
+  X(kBf16, Bf16, 64, 4)     \
+  X(kBf16, Bf16, 64, 8)     \
+  X(kF32, F32, 64, 1)       \
+  X(kF32, F32, 64, 2)       \
+  X(kF32, F32, 64, 4)       \
+  X(kF32, F32, 64, 8)
+
+int launch(int which, int dtype, int d, int G, const PodParams& p, const Plan& pl, hipStream_t s) {
+#define POD_DISPATCH(DT, E, DD, GG) \
+  if (dtype == DT && d == DD && G == GG) return launch_t<E, DD, GG>(which, p, pl, s);
+  POD_KERNEL_LIST(POD_DISPATCH)
+#undef POD_DISPATCH
+  return (int)hipErrorInvalidValue;
+}
+
+int have_kernel(int dtype, int d, int G) {
+#define POD_HAVE(DT, E, DD, GG) \
+  if (dtype == DT && d == DD && G == GG) return 1;
+  POD_KERNEL_LIST(POD_HAVE)
+#undef POD_HAVE
+  return 0;
+}
+
+}  // namespace pod

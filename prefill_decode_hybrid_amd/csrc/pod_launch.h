@@ -1,0 +1,53 @@
+// Kernel parameter block and launch entry points shared by the host runtime
+// (pod_attn.cpp) and the kernels (pod_kernels.hip).  Plain types only.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "pod_plan.h"
+
+namespace pod {
+
+struct PodParams {
+  // paged KV pool [num_pages, 16, hkv, d]
+  const void* k_pool;
+  const void* v_pool;
+  uint32_t num_pages;
+  int hq, hkv;
+  float scale_log2;  // softmax scale * log2(e): scores live in the base-2 domain
+
+  // prefill chunk
+  const void* qp;
+  void* op;
+  const int32_t* pt_p;
+  int C, P0, Lp;
+  int rows_per_tile, heads_per_tile, row_blocks, head_groups, tiles, splits, split_keys, p_tasks;
+  float* p_part;     // [task][row-head in tile][d + 2] (acc..., m, l)
+  uint32_t* p_cnt;   // [tile] arrival counters, 0 between calls
+
+  // decode batch
+  const void* qd;
+  void* od;
+  const int32_t* pt_d;
+  const int32_t* ctx;
+  int stride, N, T, d_wave_tasks, d_wg_tasks;
+  float* d_part;     // [wave task][G][d], then [G] m, [G] l
+  uint32_t* d_cnt;   // [request][kv head] arrival counters, 0 between calls
+
+  // fused launch
+  uint32_t* ctrl;     // [0] prefill queue head, [1] decode queue head, [2] claims done
+  uint32_t* tickets;  // per-CU ticket counters (never reset; the role rule is periodic)
+  int share_num, share_den, policy, grid;
+};
+
+enum { kKernelHybrid = 0, kKernelPrefill = 1, kKernelDecode = 2 };
+
+// Launch one kernel for `which` with geometry from `pl`.  Returns a hipError_t.
+int launch(int which, int dtype, int d, int G, const PodParams& p, const Plan& pl, hipStream_t s);
+
+// 1 if a kernel is built for (dtype, d, G).
+int have_kernel(int dtype, int d, int G);
+
+}  // namespace pod

@@ -1,0 +1,169 @@
+// Host-side planner; see pod_plan.h.
+#include "pod_plan.h"
+
+#include <algorithm>
+#include <cmath>
+
+#include "../../include/pod_attn.h"
+
+namespace pod {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int check_shape(const Shape& s) {
+  if (s.hq <= 0 || s.hkv <= 0 || s.d <= 0 || s.page <= 0) return POD_ERR_INVALID_ARG;
+  if (s.hq % s.hkv != 0) return POD_ERR_UNSUPPORTED;
+  const int G = s.hq / s.hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return POD_ERR_UNSUPPORTED;
+  if (s.page != kPageSize) return POD_ERR_UNSUPPORTED;
+  if (s.dtype == kBf16) {
+    if (s.d != 64 && s.d != 128) return POD_ERR_UNSUPPORTED;
+  } else if (s.dtype == kF32) {
+    if (s.d != 64) return POD_ERR_UNSUPPORTED;
+  } else {
+    return POD_ERR_UNSUPPORTED;
+  }
+  return POD_OK;
+}
+
+static void tile_geometry(const Shape& s, int& rpw, int& hpt, int& row_waves, int& rpt, int& hgroups) {
+  rpw = rows_per_wave(s.dtype);
+  hpt = std::min(s.G, kWavesPerWG);
+  row_waves = kWavesPerWG / hpt;
+  rpt = rpw * row_waves;
+  hgroups = s.G / hpt;
+}
+
+void derive_capacities(const Shape& s, Limits& lim) {
+  int rpw, hpt, rw, rpt, hg;
+  tile_geometry(s, rpw, hpt, rw, rpt, hg);
+  const int64_t slots = (int64_t)lim.num_cus * lim.wg_per_cu;
+  lim.cap_prefill_tasks = std::max<int64_t>(1, lim.cap_waves * slots);
+  lim.cap_tiles = ceil_div(std::max(1, lim.max_chunk_len), rpt) * s.hkv * hg;
+  int64_t total = lim.max_total_context > 0 ? lim.max_total_context
+                                            : (int64_t)lim.max_num_decode * lim.max_context;
+  lim.cap_wave_tasks = (int64_t)s.hkv * (lim.max_num_decode + ceil_div(total, kMinSplitTokens));
+}
+
+WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim) {
+  WorkspaceLayout w;
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  size_t at = 0;
+  w.ctrl = at;
+  at = align(at + kCtrlWords * 4);
+  w.tickets = at;
+  at = align(at + kTicketSlots * 4);
+  w.p_cnt = at;
+  at = align(at + (size_t)std::max<int64_t>(1, lim.cap_tiles) * 4);
+  w.d_cnt = at;
+  at = align(at + (size_t)std::max(1, lim.max_num_decode) * s.hkv * 4);
+  w.p_part = at;
+  const size_t rowheads = (size_t)rows_per_wave(s.dtype) * kWavesPerWG;
+  at = align(at + (size_t)lim.cap_prefill_tasks * rowheads * (s.d + 2) * 4);
+  w.d_part = at;
+  const int G = s.hq / s.hkv;
+  at = align(at + (size_t)std::max<int64_t>(1, lim.cap_wave_tasks) * G * (s.d + 2) * 4);
+  w.total = at;
+  return w;
+}
+
+static void reduce_share(int64_t a, int64_t b, int& num, int& den) {
+  // prefill share a / (a + b) as num / kShareDen, at least 1 of each role
+  double rho = (double)a / (double)(a + b);
+  num = (int)std::lround(rho * kShareDen);
+  num = std::min(kShareDen - 1, std::max(1, num));
+  den = kShareDen;
+}
+
+int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, const DecodeIn& d,
+              Plan* out) {
+  if (!out) return POD_ERR_INVALID_ARG;
+  int rc = check_shape(s);
+  if (rc) return rc;
+  Plan pl;
+  pl.mode = mode;
+  pl.num_cus = lim.num_cus;
+  pl.wg_per_cu = lim.wg_per_cu;
+  pl.policy = lim.policy;
+  if (lim.num_cus <= 0) return POD_ERR_INVALID_ARG;
+
+  bool want_p = (mode == kModeHybrid || mode == kModePrefill);
+  bool want_d = (mode == kModeHybrid || mode == kModeDecode);
+  if (mode == kModePrefill && !p.present) return POD_ERR_INVALID_ARG;
+  if (mode == kModeDecode && !d.present) return POD_ERR_INVALID_ARG;
+  if (mode == kModeHybrid && !p.present && !d.present) return POD_ERR_INVALID_ARG;
+  if (mode == kModeHybrid && !d.present) pl.fallback = 1;
+  if (mode == kModeHybrid && !p.present) pl.fallback = 2;
+  pl.has_p = want_p && p.present;
+  pl.has_d = want_d && d.present;
+
+  const int64_t slots = (int64_t)lim.num_cus * lim.wg_per_cu;
+
+  if (pl.has_p) {
+    if (p.C < 1 || p.P0 < 0) return POD_ERR_INVALID_ARG;
+    if (p.C > lim.max_chunk_len || (int64_t)p.C + p.P0 > lim.max_context) return POD_ERR_INVALID_ARG;
+    pl.C = p.C;
+    pl.P0 = p.P0;
+    pl.Lp = p.C + p.P0;
+    tile_geometry(s, pl.rows_per_wave, pl.heads_per_tile, pl.row_waves, pl.rows_per_tile,
+                  pl.head_groups);
+    pl.row_blocks = (int)ceil_div(pl.C, pl.rows_per_tile);
+    pl.tiles = pl.row_blocks * s.hkv * pl.head_groups;
+    if (pl.tiles > lim.cap_tiles) return POD_ERR_WORKSPACE;
+    const int bn = keys_per_block(s.dtype);
+    int64_t splits = 1;
+    if (pl.tiles < slots) {
+      splits = ceil_div(slots, pl.tiles);
+      splits = std::min<int64_t>(splits, lim.cap_prefill_tasks / pl.tiles);
+      splits = std::min<int64_t>(splits, ceil_div(pl.Lp, kMinPrefillSplitKeys));
+      splits = std::max<int64_t>(splits, 1);
+    }
+    pl.split_keys = (int)round_up(ceil_div(pl.Lp, splits), bn);
+    pl.splits = (int)ceil_div(pl.Lp, pl.split_keys);  // drop splits left empty by rounding
+    pl.p_tasks = pl.tiles * pl.splits;
+    if (pl.splits > 1 && pl.p_tasks > lim.cap_prefill_tasks) return POD_ERR_WORKSPACE;
+  }
+
+  if (pl.has_d) {
+    if (d.N < 1 || d.N > lim.max_num_decode || d.stride < 1 || !d.ctx_host) return POD_ERR_INVALID_ARG;
+    int64_t total = 0;
+    for (int r = 0; r < d.N; ++r) {
+      int L = d.ctx_host[r];
+      if (L < 1 || L > lim.max_context || (int64_t)L > (int64_t)d.stride * kPageSize)
+        return POD_ERR_INVALID_ARG;
+      total += L;
+    }
+    int64_t cap_total = lim.max_total_context > 0 ? lim.max_total_context
+                                                  : (int64_t)lim.max_num_decode * lim.max_context;
+    if (total > cap_total) return POD_ERR_INVALID_ARG;
+    pl.N = d.N;
+    const int64_t target = 4LL * lim.num_cus * 8;  // wave tasks: ~4 per resident wave slot
+    int64_t T = round_up(ceil_div(total * s.hkv, target), kPageSize);
+    T = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(kMinSplitTokens, T));
+    pl.T = (int)T;
+    int64_t units = 0;
+    for (int r = 0; r < d.N; ++r) units += ceil_div(d.ctx_host[r], T);
+    int64_t wt = units * s.hkv;
+    if (wt > lim.cap_wave_tasks || wt > (1LL << 30)) return POD_ERR_WORKSPACE;
+    pl.d_wave_tasks = (int)wt;
+    pl.d_wg_tasks = (int)ceil_div(wt, kWavesPerWG);
+  }
+
+  pl.grid = (pl.has_p ? pl.p_tasks : 0) + (pl.has_d ? pl.d_wg_tasks : 0);
+  if (pl.has_p && pl.has_d) {
+    if (lim.policy == kPolicyHalf) {
+      pl.share_num = 1;
+      pl.share_den = 2;
+    } else {
+      reduce_share(pl.p_tasks, pl.d_wg_tasks, pl.share_num, pl.share_den);
+    }
+  } else {
+    pl.share_num = pl.has_p ? 1 : 0;
+    pl.share_den = 1;
+  }
+  *out = pl;
+  return POD_OK;
+}
+
+}  // namespace pod

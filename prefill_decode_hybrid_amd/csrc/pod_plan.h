@@ -1,0 +1,91 @@
+// Host-side planner for hybrid-batch attention.  Plain C++17: no HIP calls,
+// so it is unit-testable on a machine without a GPU.
+//
+// A plan turns one call's shapes into the task lists the kernels walk:
+//  * prefill tiles (row block, kv head, head group), each split into KV
+//    ranges when there are too few tiles to fill the machine.  The number of
+//    prefill tasks is capped at `cap_waves` waves of resident workgroups so a
+//    chunk cannot flood the launch (paper §4.2.3 caps chunked-prefill splits
+//    at two full waves);
+//  * decode wave tasks (request, kv head, token split), one 64-lane wave each
+//    (paper §4.2.3, virtual decode CTAs of one warp), four per workgroup;
+//  * the fused launch's per-CU prefill share (paper §5.4.2: proportional
+//    allocation beats 50:50).
+#pragma once
+
+#include <cstdint>
+
+namespace pod {
+
+enum { kBf16 = 0, kF32 = 1 };
+enum { kModeHybrid = 0, kModePrefill = 1, kModeDecode = 2 };
+enum { kPolicyProportional = 0, kPolicyHalf = 1, kPolicyStatic = 2 };
+
+constexpr int kPageSize = 16;
+constexpr int kWavesPerWG = 4;
+constexpr int kMaxSplitTokens = 1024;   // one lane per page id in a 64-lane wave
+constexpr int kMinSplitTokens = 256;
+constexpr int kMinPrefillSplitKeys = 1024;
+constexpr int kShareDen = 64;
+
+struct Shape {
+  int dtype = kBf16, hq = 0, hkv = 0, G = 0, d = 0, page = kPageSize;
+};
+
+struct Limits {
+  int max_chunk_len = 0, max_num_decode = 0, max_context = 0;
+  int64_t max_total_context = 0;
+  int wg_per_cu = 2, cap_waves = 2, policy = kPolicyProportional;
+  int num_cus = 0;
+  // capacities derived by workspace_layout()
+  int64_t cap_prefill_tasks = 0, cap_wave_tasks = 0, cap_tiles = 0;
+};
+
+struct PrefillIn {
+  bool present = false;
+  int C = 0, P0 = 0;
+};
+
+struct DecodeIn {
+  bool present = false;
+  int N = 0, stride = 0;
+  const int32_t* ctx_host = nullptr;
+};
+
+struct Plan {
+  int mode = 0, fallback = 0, num_cus = 0, wg_per_cu = 0, grid = 0;
+  // prefill
+  bool has_p = false;
+  int C = 0, P0 = 0, Lp = 0;
+  int rows_per_wave = 0, heads_per_tile = 0, row_waves = 0, rows_per_tile = 0;
+  int row_blocks = 0, head_groups = 0, tiles = 0, splits = 0, split_keys = 0, p_tasks = 0;
+  // decode
+  bool has_d = false;
+  int N = 0, T = 0, d_wave_tasks = 0, d_wg_tasks = 0;
+  // fused scheduling
+  int share_num = 0, share_den = 1, policy = 0;
+};
+
+// Rows of one wave's query block and keys per staged KV block, per dtype.
+inline int rows_per_wave(int dtype) { return dtype == kBf16 ? 32 : 64; }
+inline int keys_per_block(int dtype) { return dtype == kBf16 ? 64 : 32; }
+
+// 0 if (dtype, G, d, page) is built, else the status code to return.
+int check_shape(const Shape& s);
+
+// Fill the capacity fields of `lim` for shape `s`.
+void derive_capacities(const Shape& s, Limits& lim);
+
+struct WorkspaceLayout {
+  size_t ctrl = 0, tickets = 0, p_cnt = 0, d_cnt = 0, p_part = 0, d_part = 0, total = 0;
+};
+WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim);
+
+// Validate one call and plan it.  Returns 0 or a negative pod_status.
+int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p,
+              const DecodeIn& d, Plan* out);
+
+constexpr int kTicketSlots = 2048;  // (xcc, se, sh, cu) keys
+constexpr int kCtrlWords = 64;
+
+}  // namespace pod

@@ -245,6 +245,15 @@ def make_batch(spec, seed: int = 0, with_prefill: bool = True, with_decode: bool
                        sm_scale=float(sm_scale), guard_page=guard, outlier_rows=n_out)
 
 
+def draw_context_lens(spec, seed: int = 0) -> np.ndarray:
+    """The decode context lengths make_batch(spec, seed) would draw (no pools)."""
+    if isinstance(spec, int):
+        spec = dict(CONFIGS[spec])
+    ss = np.random.SeedSequence(seed).spawn(len(_STREAMS))
+    rng = np.random.Generator(np.random.PCG64(ss[_STREAMS.index("lengths")]))
+    return _draw_lengths(spec["decode_lens"], rng)
+
+
 def describe(b: HybridBatch) -> dict:
     """Small JSON-able summary of a batch (sizes and drawn lengths)."""
     lens = [] if b.context_lens is None else b.context_lens.tolist()

@@ -1,0 +1,215 @@
+"""The C-ABI library on the CPU: symbols, argument validation and the host
+planner (no kernel is launched here)."""
+import ctypes
+import math
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import prefill_decode_hybrid_amd as pod
+from prefill_decode_hybrid_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # a non-null device pointer; planning never dereferences it
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pod.load()
+
+
+def header_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pod_\w+)\s*\(", txt, re.M))
+    return sorted(names)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(names) == set(pod.EXPORTED)
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert pod.status_string(code) not in ("", "unknown status")
+
+
+def _prefill(C, P0):
+    return pod.PodPrefillArgs(FAKE, FAKE, FAKE, C, P0)
+
+
+def _decode(lens, stride=None):
+    lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+    stride = stride or max(1, -(-int(lens.max()) // 16))
+    a = pod.PodDecodeArgs(FAKE, FAKE, FAKE, stride, FAKE, lens.ctypes.data, len(lens))
+    a._keep = lens
+    return a
+
+
+def _cfg(spec, **kw):
+    spec = dict(inputs.CONFIGS[spec]) if isinstance(spec, int) else spec
+    base = dict(dtype=pod.POD_BF16 if spec["dtype"] == "bf16" else pod.POD_F32,
+                num_q_heads=spec["num_q_heads"], num_kv_heads=spec["num_kv_heads"],
+                head_dim=spec["head_dim"], max_chunk_len=4096, max_num_decode=512,
+                max_context=32768, max_total_context=4 << 20)
+    base.update(kw)
+    return pod.make_config(**base)
+
+
+def plan(cfg, mode, pa, da, cus=256):
+    return pod.pod_attn_plan(cfg, cus, mode, pa, da)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_plan_invariants_on_configs(cid):
+    spec = inputs.CONFIGS[cid]
+    lens = inputs.draw_context_lens(cid, 0)
+    cfg = _cfg(cid)
+    C, P0 = spec["chunk_len"], spec["chunk_offset"]
+    st = plan(cfg, pod.MODE_HYBRID, _prefill(C, P0), _decode(lens))
+    hq, hkv = spec["num_q_heads"], spec["num_kv_heads"]
+    G = hq // hkv
+    # prefill tiles cover every (row, head) once
+    assert st["prefill_heads_per_tile"] == min(G, 4)
+    assert st["prefill_rows_per_tile"] * st["prefill_heads_per_tile"] == (32 if spec["dtype"] == "bf16" else 64) * 4
+    row_blocks = -(-C // st["prefill_rows_per_tile"])
+    assert st["prefill_tiles"] == row_blocks * hkv * (G // st["prefill_heads_per_tile"])
+    Lp = C + P0
+    bn = 64 if spec["dtype"] == "bf16" else 32
+    assert st["prefill_split_keys"] % bn == 0
+    assert st["prefill_splits"] * st["prefill_split_keys"] >= Lp
+    assert (st["prefill_splits"] - 1) * st["prefill_split_keys"] < Lp
+    assert st["prefill_tasks"] == st["prefill_tiles"] * st["prefill_splits"]
+    slots = 256 * st["wg_per_cu"]
+    if st["prefill_splits"] > 1:  # the split cap: at most two waves of resident workgroups
+        assert st["prefill_tasks"] <= 2 * slots
+    # decode: every (request, kv head) split into ceil(L / T) one-wave units
+    T = st["decode_split_tokens"]
+    assert T % 16 == 0 and 256 <= T <= 1024
+    assert st["decode_wave_tasks"] == hkv * sum(-(-int(L) // T) for L in lens)
+    assert st["decode_wg_tasks"] == -(-st["decode_wave_tasks"] // 4)
+    assert st["grid"] == st["prefill_tasks"] + st["decode_wg_tasks"]
+    assert 0 < st["share_num"] < st["share_den"]
+    assert st["fallback"] == 0
+
+
+def test_plan_single_role_fallbacks():
+    cfg = _cfg(2)
+    st = plan(cfg, pod.MODE_HYBRID, _prefill(100, 7), None)
+    assert st["fallback"] == 1 and st["decode_wg_tasks"] == 0 and st["grid"] == st["prefill_tasks"]
+    st = plan(cfg, pod.MODE_HYBRID, None, _decode([5, 9]))
+    assert st["fallback"] == 2 and st["prefill_tasks"] == 0 and st["grid"] == st["decode_wg_tasks"]
+
+
+def test_split_cap_limits_prefill_tasks():
+    # few tiles over a long prefix: splits fill the machine but never exceed the cap
+    cfg = _cfg(2, prefill_split_cap_waves=1)
+    st = plan(cfg, pod.MODE_PREFILL, _prefill(32, 30000), None)
+    assert st["prefill_splits"] > 1
+    assert st["prefill_tasks"] <= 1 * 256 * st["wg_per_cu"]
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(prefill=(0, 0)), pod.POD_ERR_INVALID_ARG),       # empty chunk
+    (dict(prefill=(8, -1)), pod.POD_ERR_INVALID_ARG),      # negative offset
+    (dict(prefill=(5000, 0)), pod.POD_ERR_INVALID_ARG),    # chunk above max_chunk_len
+    (dict(prefill=(100, 32700)), pod.POD_ERR_INVALID_ARG), # offset + chunk above max_context
+    (dict(decode=[0, 4]), pod.POD_ERR_INVALID_ARG),        # context 0
+    (dict(decode=[40000]), pod.POD_ERR_INVALID_ARG),       # above max_context
+    (dict(decode=[33], stride=2), pod.POD_ERR_INVALID_ARG),  # context beyond the table
+])
+def test_validation_codes(bad, code):
+    cfg = _cfg(2)
+    pa = _prefill(*bad["prefill"]) if "prefill" in bad else None
+    da = _decode(bad["decode"], bad.get("stride")) if "decode" in bad else None
+    mode = pod.MODE_PREFILL if pa is not None else pod.MODE_DECODE
+    with pytest.raises(pod.PodAttnError) as e:
+        plan(cfg, mode, pa, da)
+    assert e.value.status == code
+
+
+def test_validation_null_pointers():
+    cfg = _cfg(2)
+    pa = pod.PodPrefillArgs(None, FAKE, FAKE, 8, 0)
+    with pytest.raises(pod.PodAttnError) as e:
+        plan(cfg, pod.MODE_PREFILL, pa, None)
+    assert e.value.status == pod.POD_ERR_INVALID_ARG
+    da = _decode([5])
+    da.context_lens_host = None
+    with pytest.raises(pod.PodAttnError) as e:
+        plan(cfg, pod.MODE_DECODE, None, da)
+    assert e.value.status == pod.POD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=96), dict(num_q_heads=24, num_kv_heads=8),
+                                dict(page_size=8), dict(dtype=pod.POD_F32, head_dim=128),
+                                dict(num_q_heads=32, num_kv_heads=2), dict(wg_per_cu=4)])
+def test_unsupported_shapes(kw):
+    cfg = _cfg(2, **kw)
+    with pytest.raises(pod.PodAttnError) as e:
+        plan(cfg, pod.MODE_DECODE, None, _decode([5]))
+    assert e.value.status == pod.POD_ERR_UNSUPPORTED
+
+
+def test_workspace_limit():
+    cfg = _cfg(2, max_total_context=1000)
+    with pytest.raises(pod.PodAttnError) as e:
+        plan(cfg, pod.MODE_DECODE, None, _decode([800, 800]))
+    assert e.value.status == pod.POD_ERR_INVALID_ARG
+
+
+def test_create_without_gpu_fails_cleanly(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p()
+    rc = lib.pod_attn_create(ctypes.byref(_cfg(2)), ctypes.byref(h))
+    assert rc == pod.POD_ERR_HIP and not h.value
+
+
+def simulate_fused_claims(n_p, n_d, num, den, n_cus, seed):
+    """Host model of the fused kernel's role pick and queue claims under a random
+    arrival order and random CU placement: returns the claimed (role, task) list."""
+    rng = random.Random(seed)
+    tickets = [0] * n_cus
+    heads = [0, 0]
+    lim = [n_p, n_d]
+    claims = []
+    for _ in range(n_p + n_d):
+        cu = rng.randrange(n_cus)
+        t = tickets[cu] % den
+        tickets[cu] += 1
+        role = 0 if ((t + 1) * num + den - 1) // den > (t * num + den - 1) // den else 1
+        x = heads[role]
+        heads[role] += 1
+        if x >= lim[role]:
+            role ^= 1
+            x = heads[role]
+            heads[role] += 1
+        claims.append((role, x))
+    return claims
+
+
+@pytest.mark.parametrize("n_p,n_d,num,den", [(256, 2048, 7, 64), (1, 5, 1, 2), (40, 3, 63, 64),
+                                             (100, 100, 32, 64), (5, 1000, 1, 64)])
+def test_fused_claims_cover_every_task_once(n_p, n_d, num, den):
+    for seed in range(20):
+        claims = simulate_fused_claims(n_p, n_d, num, den, n_cus=8, seed=seed)
+        p = sorted(x for r, x in claims if r == 0)
+        d = sorted(x for r, x in claims if r == 1)
+        assert p == list(range(n_p)) and d == list(range(n_d))
+
+
+def test_role_rule_is_proportional_and_prefill_first():
+    for num, den in [(1, 9), (7, 64), (1, 2), (63, 64)]:
+        roles = [((t + 1) * num + den - 1) // den > (t * num + den - 1) // den for t in range(den)]
+        assert sum(roles) == num and roles[0]

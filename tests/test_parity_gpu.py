@@ -1,0 +1,148 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every entry point (pod_attn_hybrid, pod_attn_prefill_only,
+pod_attn_decode_only) is compared element by element with the oracle on the
+same seeded inputs.  Bars: bf16 inputs with fp32 accumulation, max abs error
+<= 2e-2 and mean abs error <= 2e-3; fp32 inputs, max abs error <= 1e-4.
+Small cases span several tiles and ragged tails and are compared in full; the
+five workload configs are compared in full (1, 2) or on sampled rows and
+requests (3, 4, 5: first/last rows, every tile edge, random rows; the
+shortest and longest requests plus random ones) in the launch configuration
+the benchmark times.  Fusion must not change the result: the fused call is
+bitwise equal to the two split calls, and repeated calls are bitwise equal.
+"""
+import numpy as np
+import pytest
+import torch
+
+import prefill_decode_hybrid_amd as pod
+from prefill_decode_hybrid_amd import inputs
+from gpu_helpers import Run, check_against_oracle, sample_reqs, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pod.load()
+
+
+def spec(dtype, hq, hkv, d, C, P0, lens, outliers=0.0, contiguous=False):
+    return dict(name=f"{dtype}_h{hq}x{hkv}_d{d}_C{C}_P{P0}", dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                head_dim=d, chunk_len=C, chunk_offset=P0, decode_lens=list(lens), contiguous=contiguous,
+                k_outlier_frac=outliers)
+
+
+SMALL = [
+    spec("bf16", 8, 2, 128, 77, 300, [1, 15, 16, 17, 300, 1023, 1025, 2100]),
+    spec("bf16", 16, 2, 128, 40, 0, [5, 64, 2000], outliers=0.02),
+    spec("bf16", 4, 4, 64, 130, 17, [33, 700]),
+    spec("bf16", 8, 4, 64, 1, 5000, [1, 4096]),
+    spec("bf16", 8, 2, 128, 64, 12000, [20000]),           # prefill and decode splits + merges
+    spec("f32", 8, 2, 64, 100, 29, [3, 999]),
+    spec("f32", 2, 2, 64, 64, 2000, [1500, 1]),
+    spec("f32", 16, 2, 64, 70, 3000, [4000, 17]),
+]
+
+
+@pytest.mark.parametrize("sp", SMALL, ids=lambda s: s["name"])
+def test_small_cases(sp):
+    say(f"case {sp['name']}")
+    run = Run(inputs.make_batch(sp, seed=1))
+    try:
+        op, od = run.hybrid()
+        check_against_oracle(run, op, od, label="hybrid")
+        sp_, sd_ = run.separate()
+        check_against_oracle(run, sp_, sd_, label="separate")
+        assert torch.equal(op, sp_) and torch.equal(od, sd_), "fused result differs from split launches"
+        op2, od2 = run.hybrid()
+        assert torch.equal(op, op2) and torch.equal(od, od2), "hybrid not run-to-run deterministic"
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("policy", [pod.POD_POLICY_HALF, pod.POD_POLICY_STATIC])
+def test_policies_give_identical_results(policy):
+    sp = SMALL[0]
+    base = Run(inputs.make_batch(sp, seed=2))
+    alt = Run(inputs.make_batch(sp, seed=2), policy=policy)
+    try:
+        a = base.hybrid()
+        b = alt.hybrid()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    finally:
+        base.close()
+        alt.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_key_is_exact(dtype):
+    # decode over one key and prefill row 0 at offset 0 return that V row bit for bit
+    sp = spec(dtype, 8, 2, 64 if dtype == "f32" else 128, 33, 0, [1, 1, 2])
+    run = Run(inputs.make_batch(sp, seed=3))
+    try:
+        op, od = run.hybrid()
+        b = run.cpu
+        G = b.num_q_heads // b.num_kv_heads
+        for r in (0, 1):
+            page = int(b.page_table_decode[r, 0])
+            v0 = b.v_pool[page, 0].repeat_interleave(G, dim=0)
+            assert torch.equal(od[r].cpu(), v0)
+        page = int(b.page_table_prefill[0])
+        assert torch.equal(op[0].cpu(), b.v_pool[page, 0].repeat_interleave(G, dim=0))
+    finally:
+        run.close()
+
+
+def test_hybrid_with_one_half_missing():
+    run = Run(inputs.make_batch(SMALL[0], seed=4))
+    try:
+        b = run.dev
+        op, od = run.outputs()
+        pa, da = run.att.args(b, op, od, run.ctx_host)
+        pod.pod_attn_hybrid(run.att.h, b.k_pool, b.v_pool, pa, None)
+        assert run.att.stats()["fallback"] == 1
+        pod.pod_attn_hybrid(run.att.h, b.k_pool, b.v_pool, None, da)
+        assert run.att.stats()["fallback"] == 2
+        torch.cuda.synchronize()
+        check_against_oracle(run, op, od, label="single-role hybrid")
+    finally:
+        run.close()
+
+
+_CACHE = {}
+
+
+def config_run(cid):
+    if cid not in _CACHE:
+        _CACHE.clear()
+        torch.cuda.empty_cache()
+        say(f"generating config {cid}")
+        _CACHE[cid] = Run(inputs.make_batch(cid, seed=0))
+    return _CACHE[cid]
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_config_full(cid):
+    run = config_run(cid)
+    op, od = run.hybrid()
+    say(f"config {cid} plan {run.att.stats()}")
+    check_against_oracle(run, op, od, label=f"config {cid} hybrid")
+    sp_, sd_ = run.separate()
+    check_against_oracle(run, sp_, sd_, label=f"config {cid} separate")
+    assert torch.equal(op, sp_) and torch.equal(od, sd_)
+
+
+@pytest.mark.parametrize("cid", [3, 4, 5])
+def test_config_sampled(cid):
+    run = config_run(cid)
+    op, od = run.hybrid()
+    say(f"config {cid} plan {run.att.stats()}")
+    rows = sample_rows(run.cpu.chunk_len)
+    reqs = sample_reqs(run.cpu.context_lens.numpy())
+    check_against_oracle(run, op, od, rows=rows, reqs=reqs, label=f"config {cid} hybrid")
+    assert torch.isfinite(op.float()).all() and torch.isfinite(od.float()).all()
+    sp_, sd_ = run.separate()
+    assert torch.equal(op, sp_) and torch.equal(od, sd_), "fused result differs from split launches"
