@@ -183,11 +183,12 @@ def main():
 
     # untimed check: fusion leaves the result bit-identical to the split launches
     fused()
+    torch.cuda.synchronize()
+    plan = att.stats()
     serial()
     torch.cuda.synchronize()
     same = bool(torch.equal(op, op2) and torch.equal(od, od2))
     finite = bool(torch.isfinite(op.float()).all() and torch.isfinite(od.float()).all())
-    plan = att.stats()
     log(f"[bench] plan {plan}; fused==split {same}; finite {finite}")
 
     for _ in range(args.warmup):

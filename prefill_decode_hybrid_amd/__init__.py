@@ -216,9 +216,9 @@ class PodAttention:
     @staticmethod
     def args(batch, o_prefill, o_decode, ctx_host):
         pa = da = None
-        if batch.q_prefill is not None:
+        if batch.q_prefill is not None and o_prefill is not None:
             pa = prefill_args(batch.q_prefill, o_prefill, batch.page_table_prefill, batch.chunk_offset)
-        if batch.q_decode is not None:
+        if batch.q_decode is not None and o_decode is not None:
             da = decode_args(batch.q_decode, o_decode, batch.page_table_decode, batch.context_lens, ctx_host)
         return pa, da
 
