@@ -212,6 +212,42 @@ DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S) {
   return false;
 }
 
+// Count this split's arrival at (r, g); the last of the S splits merges all
+// partials of (r, g) in split order and restores the counter to zero.
+template <class E, int D, int G>
+DEV void decode_finish(const PodParams& p, int r, int s, int S, int unit, int g) {
+  const int lane = lane_id();
+  const int hkv = p.hkv;
+  uint32_t* cnt = p.d_cnt + (int64_t)r * hkv + g;
+  if (!arrive_last(cnt, (uint32_t)S)) return;
+
+  // last split merges all S partials of (r, g) in split order
+  const int unit0 = unit - s;
+  constexpr int MPL = D / 64;
+  for (int h = 0; h < G; ++h) {
+    float M = kNegInf;
+    for (int ss = 0; ss < S; ++ss) {
+      const float* ps = p.d_part + ((int64_t)(unit0 + ss) * hkv + g) * G * (D + 2);
+      M = fmaxf(M, ps[G * D + h]);
+    }
+    const float Mu = safe_max(M);
+    float a[MPL] = {};
+    float Lsum = 0.0f;
+    for (int ss = 0; ss < S; ++ss) {
+      const float* ps = p.d_part + ((int64_t)(unit0 + ss) * hkv + g) * G * (D + 2);
+      const float w = fast_exp2(ps[G * D + h] - Mu);
+      Lsum += w * ps[G * D + G + h];
+#pragma unroll
+      for (int e = 0; e < MPL; ++e) a[e] += w * ps[h * D + lane * MPL + e];
+    }
+    const float inv = 1.0f / Lsum;
+    const int64_t o = ((int64_t)r * p.hq + (int64_t)g * G + h) * D + lane * MPL;
+#pragma unroll
+    for (int e = 0; e < MPL; ++e) store_out<E>(p.od, o + e, a[e] * inv);
+  }
+  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <class E, int D, int G, int PF>
 DEV void decode_wave(const PodParams& p, int wt) {
   using Fr = DecFrag<E, D>;
@@ -260,7 +296,7 @@ DEV void decode_wave(const PodParams& p, int wt) {
   constexpr int NB = PF + 1;
   uint32_t kr[NB][4][DW], vr[NB][4][DW];
 
-  auto issue = [&](uint32_t (&kd)[4][DW], uint32_t (&vd)[4][DW], int i) {
+  auto issue = [&](uint32_t (&kd)[4][DW], uint32_t (&vd)[4][DW], int i) __attribute__((always_inline)) {
     const int64_t page = __builtin_amdgcn_readlane(pid, i);
     const int64_t off = page * page_bytes;
 #pragma unroll
@@ -269,7 +305,7 @@ DEV void decode_wave(const PodParams& p, int wt) {
     for (int u = 0; u < 4; ++u) load_dw<DW>(vd[u], vb + off + 4 * u * tok_bytes);
   };
 
-  auto consume = [&](const uint32_t (&kd)[4][DW], const uint32_t (&vd)[4][DW], int i) {
+  auto consume = [&](const uint32_t (&kd)[4][DW], const uint32_t (&vd)[4][DW], int i) __attribute__((always_inline)) {
     const int tb = t0 + i * kPageSize + slot;
     float sc[4][G];
 #pragma unroll
@@ -373,40 +409,224 @@ DEV void decode_wave(const PodParams& p, int wt) {
       }
     }
   }
-  uint32_t* cnt = p.d_cnt + (int64_t)r * hkv + g;
-  if (!arrive_last(cnt, (uint32_t)S)) return;
+  decode_finish<E, D, G>(p, r, s, S, unit, g);
+}
 
-  // last split merges all S partials of (r, g) in split order
-  const int unit0 = unit - s;
-  constexpr int MPL = D / 64;
-  for (int h = 0; h < G; ++h) {
-    float M = kNegInf;
-    for (int ss = 0; ss < S; ++ss) {
-      const float* ps = p.d_part + ((int64_t)(unit0 + ss) * hkv + g) * G * (D + 2);
-      M = fmaxf(M, ps[G * D + h]);
-    }
-    const float Mu = safe_max(M);
-    float a[MPL] = {};
-    float Lsum = 0.0f;
-    for (int ss = 0; ss < S; ++ss) {
-      const float* ps = p.d_part + ((int64_t)(unit0 + ss) * hkv + g) * G * (D + 2);
-      const float w = fast_exp2(ps[G * D + h] - Mu);
-      Lsum += w * ps[G * D + G + h];
+// bf16 decode on MFMA (v_mfma_f32_16x16x32_bf16), 16 query-head columns of
+// which the G heads of kv head g are used.  Per pair of pages (32 keys):
+//   S^T[key, head] = K Q^T     A = K rows straight from HBM (lane: key l%16,
+//                              8 d-elements at 8*(l/16) of each 32-d chunk),
+//                              B = Q^T held in registers;
+//   O^T[d, head] += V^T P^T    A = V^T read from this wave's LDS copy of the
+//                              two V pages with ds_read_b64_tr_b16 (the
+//                              transposing LDS read), B = P^T straight from
+//                              the S^T accumulators.
+// The key order inside an MFMA step is permuted identically on both sides
+// (lane quad q feeds keys 4q..4q+3 of each page), so no data is reshuffled.
+// The softmax maximum is raised only when a score exceeds it by more than
+// 2^8 (base-2 units of 8); exp2(s - m) <= 256 then, and the final division
+// by l is unchanged, so the result is the same exact softmax.
+template <int D>
+struct DecMfma {
+  static constexpr int KC = D / 32;          // QK k-chunks
+  static constexpr int DB = D / 16;          // PV d-blocks
+  static constexpr int VROW = D * 2 + 32;    // LDS row stride (bytes), padded
+  static constexpr int LDS_WAVE = 32 * VROW; // two pages of V per wave
+  static constexpr float kLazy = 8.0f;
+};
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int D, int G>
+DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
+  using C = DecMfma<D>;
+  constexpr int KC = C::KC, DB = C::DB;
+  const int lane = lane_id();
+  const int hkv = p.hkv;
+  const int g = wt % hkv;
+  const int unit = wt / hkv;
+  int r, s, S;
+  if (!locate_unit(p, unit, r, s, S)) return;
+  r = __builtin_amdgcn_readfirstlane(r);
+  s = __builtin_amdgcn_readfirstlane(s);
+  S = __builtin_amdgcn_readfirstlane(S);
+  const int L = min(p.ctx[r], p.stride * kPageSize);
+  const int t0 = s * p.T;
+  const int t1 = min(t0 + p.T, L);
+  const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
+  const int npair = (npg + 1) >> 1;
+  const int kk = lane & 15, dq = lane >> 4;   // load role: key in page, 8-element quarter
+
+  int pid = 0;
+  if (lane < npg) pid = p.pt_d[(int64_t)r * p.stride + t0 / kPageSize + lane];
+  pid = (int)min((uint32_t)pid, p.num_pages - 1u);
+
+  // Q^T operand: column = head kk (< G), rows d = 32c + 8dq .. +8
+  bf16x8_t qf[KC];
+  {
+    const char* qb = reinterpret_cast<const char*>(p.qd) +
+                     (((int64_t)r * p.hq + (int64_t)g * G + kk) * D + 8 * dq) * 2;
 #pragma unroll
-      for (int e = 0; e < MPL; ++e) a[e] += w * ps[h * D + lane * MPL + e];
+    for (int c = 0; c < KC; ++c) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kk < G) v = *reinterpret_cast<const uint4*>(qb + c * 64);
+      qf[c] = as_bf16x8(v);
     }
-    const float inv = 1.0f / Lsum;
-    const int64_t o = ((int64_t)r * p.hq + (int64_t)g * G + h) * D + lane * MPL;
-#pragma unroll
-    for (int e = 0; e < MPL; ++e) store_out<E>(p.od, o + e, a[e] * inv);
   }
-  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t tok_bytes = (int64_t)hkv * D * 2;
+  const int64_t page_bytes = kPageSize * tok_bytes;
+  const int64_t lane_off = (int64_t)kk * tok_bytes + ((int64_t)g * D + 8 * dq) * 2;
+  const char* kb = reinterpret_cast<const char*>(p.k_pool) + lane_off;
+  const char* vb = reinterpret_cast<const char*>(p.v_pool) + lane_off;
+
+  f32x4_t acc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) acc[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.0f;
+
+  u32x4_t kr[2][2][KC], vr[2][2][KC];
+  auto issue = [&](u32x4_t (&kd)[2][KC], u32x4_t (&vd)[2][KC], int pair) __attribute__((always_inline)) {
+    // A missing second page (odd page count) re-reads the last page; every key
+    // past t1 is masked in consume(), so its values never reach the result.
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const int pg = min(2 * pair + pp, npg - 1);
+      const int64_t off = (int64_t)__builtin_amdgcn_readlane(pid, pg) * page_bytes;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kd[pp][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + off + c * 64));
+#pragma unroll
+      for (int c = 0; c < KC; ++c) vd[pp][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + off + c * 64));
+    }
+  };
+
+  const int hq4 = lane >> 4;  // MFMA output role: keys 4*hq4 .. +4 of each page
+  auto consume = [&](const u32x4_t (&kd)[2][KC], const u32x4_t (&vd)[2][KC], int pair) __attribute__((always_inline)) {
+    const int kbase = t0 + 32 * pair;
+    // V pages -> LDS (rows = keys), invisible keys zeroed
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const bool ok = kbase + 16 * pp + kk < t1;
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        *reinterpret_cast<u32x4_t*>(lds + (16 * pp + kk) * C::VROW + (32 * c + 8 * dq) * 2) =
+            ok ? vd[pp][c] : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+    // S^T for both pages
+    f32x4_t sc[2];
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      sc[pp] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        sc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kd[pp][c]), qf[c], sc[pp], 0, 0, 0);
+    }
+    float mloc = kNegInf;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = kbase + 16 * pp + 4 * hq4 + i < t1;
+        const float v = ok ? sc[pp][i] * p.scale_log2 : kNegInf;
+        sc[pp][i] = v;
+        mloc = fmaxf(mloc, v);
+      }
+    if (__builtin_amdgcn_ballot_w64(mloc > m + C::kLazy) != 0) {
+      float mm = fmaxf(mloc, xor_lane(mloc, 16));
+      mm = fmaxf(mm, xor_lane(mm, 32));
+      const float mnew = fmaxf(m, mm);
+      const float alpha = fast_exp2(m - safe_max(mnew));
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) acc[b] *= alpha;
+      m = mnew;
+    }
+    const float mu = safe_max(m);
+    uint32_t pw[4];
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const float e0 = fast_exp2(sc[pp][0] - mu), e1 = fast_exp2(sc[pp][1] - mu);
+      const float e2 = fast_exp2(sc[pp][2] - mu), e3 = fast_exp2(sc[pp][3] - mu);
+      l += (e0 + e1) + (e2 + e3);
+      pw[2 * pp] = pack_bf16(e0, e1);
+      pw[2 * pp + 1] = pack_bf16(e2, e3);
+    }
+    const bf16x8_t pf = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    // O^T += V^T P^T; lane (quad hq4, i = 4k + j) reads keys 4*hq4 + k, d = 16b + 4j .. +4
+    const int tk = (lane & 15) >> 2, tj = lane & 3;
+    const char* tr0 = lds + (4 * hq4 + tk) * C::VROW + 4 * tj * 2;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(tr0 + 32 * b));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(tr0 + 16 * C::VROW + 32 * b));
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (short __attribute__((ext_vector_type(8)))){
+          lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc[b], 0, 0, 0);
+    }
+  };
+
+  // Double-buffered software pipeline with a straight-line steady state, so
+  // the wait for one buffer's loads leaves the other buffer's loads in flight.
+  issue(kr[0], vr[0], 0);
+  int i = 0;
+  for (; i + 2 < npair; i += 2) {
+    issue(kr[1], vr[1], i + 1);
+    consume(kr[0], vr[0], i);
+    issue(kr[0], vr[0], i + 2);
+    consume(kr[1], vr[1], i + 1);
+  }
+  if (i + 1 < npair) {
+    issue(kr[1], vr[1], i + 1);
+    consume(kr[0], vr[0], i);
+    consume(kr[1], vr[1], i + 1);
+  } else {
+    consume(kr[0], vr[0], i);
+  }
+
+  // l over the four key quads of each head column
+  l += xor_lane(l, 16);
+  l += xor_lane(l, 32);
+  const int h = lane & 15;
+  if (S == 1) {
+    if (h < G) {
+      const float inv = 1.0f / l;
+      char* orow = reinterpret_cast<char*>(p.od) + (((int64_t)r * p.hq + (int64_t)g * G + h) * D + 4 * hq4) * 2;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        uint2 w;
+        w.x = pack_bf16(acc[b][0] * inv, acc[b][1] * inv);
+        w.y = pack_bf16(acc[b][2] * inv, acc[b][3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * b) = w;
+      }
+    }
+    return;
+  }
+  float* part = p.d_part + (int64_t)wt * G * (D + 2);
+  if (h < G) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+      *reinterpret_cast<float4*>(part + h * D + 16 * b + 4 * hq4) = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    if (hq4 == 0) {
+      part[G * D + h] = m;
+      part[G * D + G + h] = l;
+    }
+  }
+  decode_finish<Bf16, D, G>(p, r, s, S, unit, g);
 }
 
 template <class E, int D, int G, int PF>
-DEV void decode_wg(const PodParams& p, int wg_task) {
+DEV void decode_wg(const PodParams& p, int wg_task, char* smem) {
   const int wt = wg_task * kWavesPerWG + wave_id();
-  if (wt < p.d_wave_tasks) decode_wave<E, D, G, PF>(p, wt);
+  if (wt >= p.d_wave_tasks) return;
+  if constexpr (E::bytes == 2)
+    decode_wave_mfma<D, G>(p, wt, smem + wave_id() * DecMfma<D>::LDS_WAVE);
+  else
+    decode_wave<E, D, G, PF>(p, wt);
 }
 
 // ---------------------------------------------------------- prefill (a2, a4)
@@ -456,7 +676,8 @@ struct PfBf16 {
   static constexpr int VSTR = (BN + 8) * 2;           // V^T row stride (bytes), padded
   static constexpr int KBYTES = BN * KSTR;
   static constexpr int STAGE = KBYTES + D * VSTR;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int PIDS = kMaxSplitKeys / kPageSize;   // page ids of one split
+  static constexpr int LDS = 2 * STAGE + PIDS * 4;
   static constexpr int CH = D / 8;                    // 16-byte chunks per key row
   static constexpr int KLOADS = CH / 4;               // K chunks per thread per block
 };
@@ -465,8 +686,13 @@ struct PfBf16 {
 // the 8 keys one MFMA lane feeds for P^T are contiguous (see prefill_tile).
 DEV int vt_pos(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
 
+// Copy the physical ids of pages [pg0, pg0 + n) into LDS (clamped into the pool).
+DEV void preload_page_ids(const PodParams& p, int pg0, int n, int* pids) {
+  for (int i = threadIdx.x; i < n; i += 256) pids[i] = (int)min((uint32_t)p.pt_p[pg0 + i], p.num_pages - 1u);
+}
+
 template <int D>
-DEV void stage_load_bf16(const PodParams& p, int kb0, uint4 (&kreg)[PfBf16<D>::KLOADS], uint4 (&vreg)[4]) {
+DEV void stage_load_bf16(const PodParams& p, const int* pids, int pg0, int kb0, uint4 (&kreg)[PfBf16<D>::KLOADS], uint4 (&vreg)[4]) {
   using C = PfBf16<D>;
   const int tid = threadIdx.x;
   const int64_t tok_bytes = (int64_t)p.hkv * D * 2;
@@ -477,7 +703,7 @@ DEV void stage_load_bf16(const PodParams& p, int kb0, uint4 (&kreg)[PfBf16<D>::K
     const int c = idx % C::CH;
     kreg[i] = make_uint4(0, 0, 0, 0);
     if (key < p.Lp) {
-      const int64_t page = min((uint32_t)p.pt_p[key >> 4], p.num_pages - 1u);
+      const int64_t page = pids[(key >> 4) - pg0];
       const char* src = reinterpret_cast<const char*>(p.k_pool) + (page * kPageSize + (key & 15)) * tok_bytes + c * 16;
       kreg[i] = *reinterpret_cast<const uint4*>(src);
     }
@@ -489,7 +715,7 @@ DEV void stage_load_bf16(const PodParams& p, int kb0, uint4 (&kreg)[PfBf16<D>::K
       const int key = kb0 + 4 * kq + i;
       vreg[i] = make_uint4(0, 0, 0, 0);
       if (key < p.Lp) {
-        const int64_t page = min((uint32_t)p.pt_p[key >> 4], p.num_pages - 1u);
+        const int64_t page = pids[(key >> 4) - pg0];
         const char* src = reinterpret_cast<const char*>(p.v_pool) + (page * kPageSize + (key & 15)) * tok_bytes + c * 16;
         vreg[i] = *reinterpret_cast<const uint4*>(src);
       }
@@ -588,16 +814,23 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, char* smem, int* flag) 
   const int nblk = t.k1 > t.k0 ? (t.k1 - t.k0 + C::BN - 1) / C::BN : 0;
   const int lim = p.P0 + row;  // last visible key of this lane's row
 
+  // page ids of every block of this split (keys past Lp are never loaded)
+  int* pids = reinterpret_cast<int*>(smem + 2 * C::STAGE);
+  const int pg0 = t.k0 / kPageSize;
+  const int pg1 = min((p.Lp + kPageSize - 1) / kPageSize, (t.k0 + nblk * C::BN) / kPageSize);
+  preload_page_ids(p, pg0, pg1 - pg0, pids);
+  __syncthreads();
+
   uint4 kreg[C::KLOADS], vreg[4];
   if (nblk > 0) {
-    stage_load_bf16<D>(pk, t.k0, kreg, vreg);
+    stage_load_bf16<D>(pk, pids, pg0, t.k0, kreg, vreg);
     stage_store_bf16<D>(smem, kreg, vreg);
   }
   __syncthreads();
   for (int b = 0; b < nblk; ++b) {
     const int kb0 = t.k0 + b * C::BN;
     char* st = smem + (b & 1) * C::STAGE;
-    if (b + 1 < nblk) stage_load_bf16<D>(pk, kb0 + C::BN, kreg, vreg);
+    if (b + 1 < nblk) stage_load_bf16<D>(pk, pids, pg0, kb0 + C::BN, kreg, vreg);
     if (kb0 < t.kw) {
       // ---- scores S^T (keys x rows), two 32-key tiles
       f32x16_t sc[2];
@@ -826,11 +1059,12 @@ struct PfSel<F32, D> {
 // ------------------------------------------------------------------ kernels
 // Pages in flight per decode wave: the fused kernel keeps 2 WGs per CU, so its
 // decode waves prefetch deeper; the decode-only kernel runs more waves instead.
-template <int G>
-constexpr int fused_pf() { return G >= 8 ? 1 : 2; }
-constexpr int kDecodePF = 1;
-template <int G>
-constexpr int decode_min_blocks() { return G >= 4 ? 2 : 4; }  // VGPR budget 256 / 128
+template <class E, int G>
+constexpr int fused_pf() { return E::bytes == 2 ? 1 : (G >= 8 ? 1 : 2); }  // bf16: pairs of pages
+template <class E>
+constexpr int decode_pf() { return 1; }
+template <class E, int G>
+constexpr int decode_min_blocks() { return E::bytes == 2 ? 2 : (G >= 4 ? 2 : 4); }
 
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(PodParams p) {
@@ -839,9 +1073,13 @@ __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(PodParams p) {
   PfSel<E, D>::run(p, blockIdx.x, smem, &flag);
 }
 
+template <class E, int D>
+constexpr int decode_lds() { return E::bytes == 2 ? kWavesPerWG * DecMfma<D>::LDS_WAVE : 16; }
+
 template <class E, int D, int G>
-__global__ __launch_bounds__(256, decode_min_blocks<G>()) void pod_decode_kernel(PodParams p) {
-  decode_wg<E, D, G, kDecodePF>(p, blockIdx.x);
+__global__ __launch_bounds__(256, (decode_min_blocks<E, G>())) void pod_decode_kernel(PodParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[decode_lds<E, D>()];
+  decode_wg<E, D, G, decode_pf<E>()>(p, blockIdx.x, smem);
 }
 
 // Fused hybrid kernel.  Each workgroup takes a ticket on its CU's counter;
@@ -888,7 +1126,7 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   if (role == 0) {
     if (task < p.p_tasks) PfSel<E, D>::run(p, task, smem, &flag);
   } else {
-    if (task < p.d_wg_tasks) decode_wg<E, D, G, fused_pf<G>()>(p, task);
+    if (task < p.d_wg_tasks) decode_wg<E, D, G, fused_pf<E, G>()>(p, task, smem);
   }
 }
 

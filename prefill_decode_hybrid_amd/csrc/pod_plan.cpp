@@ -39,8 +39,9 @@ void derive_capacities(const Shape& s, Limits& lim) {
   int rpw, hpt, rw, rpt, hg;
   tile_geometry(s, rpw, hpt, rw, rpt, hg);
   const int64_t slots = (int64_t)lim.num_cus * lim.wg_per_cu;
-  lim.cap_prefill_tasks = std::max<int64_t>(1, lim.cap_waves * slots);
   lim.cap_tiles = ceil_div(std::max(1, lim.max_chunk_len), rpt) * s.hkv * hg;
+  lim.cap_prefill_tasks = std::max<int64_t>(
+      {1, lim.cap_waves * slots, lim.cap_tiles * ceil_div(std::max(1, lim.max_context), kMaxSplitKeys)});
   int64_t total = lim.max_total_context > 0 ? lim.max_total_context
                                             : (int64_t)lim.max_num_decode * lim.max_context;
   lim.cap_wave_tasks = (int64_t)s.hkv * (lim.max_num_decode + ceil_div(total, kMinSplitTokens));
@@ -119,10 +120,12 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
       splits = std::min<int64_t>(splits, ceil_div(pl.Lp, kMinPrefillSplitKeys));
       splits = std::max<int64_t>(splits, 1);
     }
+    splits = std::max<int64_t>(splits, ceil_div(pl.Lp, kMaxSplitKeys));
     pl.split_keys = (int)round_up(ceil_div(pl.Lp, splits), bn);
     pl.splits = (int)ceil_div(pl.Lp, pl.split_keys);  // drop splits left empty by rounding
     pl.p_tasks = pl.tiles * pl.splits;
     if (pl.splits > 1 && pl.p_tasks > lim.cap_prefill_tasks) return POD_ERR_WORKSPACE;
+    if (pl.split_keys > kMaxSplitKeys) return POD_ERR_WORKSPACE;
   }
 
   if (pl.has_d) {

@@ -26,6 +26,7 @@ constexpr int kWavesPerWG = 4;
 constexpr int kMaxSplitTokens = 1024;   // one lane per page id in a 64-lane wave
 constexpr int kMinSplitTokens = 256;
 constexpr int kMinPrefillSplitKeys = 1024;
+constexpr int kMaxSplitKeys = 32768;       // page ids of one split are staged in LDS
 constexpr int kShareDen = 64;
 
 struct Shape {
