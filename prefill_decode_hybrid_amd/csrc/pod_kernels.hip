@@ -133,39 +133,86 @@ DEV void store_out(void* base, int64_t idx, float v) {
   }
 }
 
-// Merge S split partials (acc, m, l) of one output row-head, in split order,
-// and store the normalised row.  part(s) points at split s's [d + 2] block
-// (acc[0..d), m, l) with stride `sstride` floats.  64 lanes cover d.
+// Split partials cross compute units on different XCDs, whose L2s are not
+// coherent with each other.  They are written and read with device-scope
+// accesses (sc1: written through to, and read from, the device coherence
+// point), so publishing them needs no L2 writeback or invalidate: a wave
+// waits until its device-scope stores have completed (vmcnt 0) and only then
+// bumps the arrival counter, and the last arriver reads them back with
+// device-scope loads after its counter update has returned.
+DEV void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV void st_dev4(float* p, float a, float b, float c, float d) {
+  st_dev(p, a);
+  st_dev(p + 1, b);
+  st_dev(p + 2, c);
+  st_dev(p + 3, d);
+}
+// Wait until every vector memory operation this wave issued has completed.
+DEV void wait_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+DEV float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+DEV float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Merge the S split partials of one output row-head and store the row.
+// Split s lives at part0 + s * sstride: acc[0..D) unnormalised, m (base 2) at
+// +moff, l at +loff.  Weights w_s = 2^(m_s - max m) are formed one split per
+// lane; the weighted sum runs over the splits in index order (64 lanes cover
+// d), so the result does not depend on which split arrived last.
 template <class E, int D>
-DEV void merge_row(const float* part0, int64_t sstride, int S, void* out, int64_t out_off) {
+DEV void merge_partials(const float* part0, int64_t sstride, int moff, int loff, int S, void* out,
+                        int64_t out_off) {
   constexpr int EPL = D / 64;
   const int lane = lane_id();
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part0[s * sstride + D]);
-  const float Mu = safe_max(M);
+  for (int s0 = 0; s0 < S; s0 += 64)
+    if (s0 + lane < S) M = fmaxf(M, ld_dev(part0 + (int64_t)(s0 + lane) * sstride + moff));
+  const float Mu = safe_max(wave_max(M));
   float acc[EPL] = {};
   float L = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float* ps = part0 + s * sstride;
-    const float w = fast_exp2(ps[D] - Mu);
-    L += w * ps[D + 1];
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    float w = 0.0f;
+    if (s0 + lane < S) {
+      const float* ps = part0 + (int64_t)(s0 + lane) * sstride;
+      w = fast_exp2(ld_dev(ps + moff) - Mu);
+      L += w * ld_dev(ps + loff);
+    }
+    const int n = min(64, S - s0);
+#pragma unroll 4
+    for (int k = 0; k < n; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+      const float* ps = part0 + (int64_t)(s0 + k) * sstride + lane * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += w * ps[lane * EPL + e];
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wk, ld_dev(ps + e), acc[e]);
+    }
   }
-  const float inv = 1.0f / L;
+  const float inv = 1.0f / wave_sum(L);
 #pragma unroll
   for (int e = 0; e < EPL; ++e) store_out<E>(out, out_off + lane * EPL + e, acc[e] * inv);
 }
 
-// Release this wave's stores, count an arrival, report whether it was the last.
+// Count this wave's arrival after its partial stores completed; true for the
+// last of `expected` arrivals.
 DEV bool arrive_last(uint32_t* counter, uint32_t expected) {
   uint32_t old = 0;
-  __threadfence();
+  wait_vmem();
   if (lane_id() == 0) old = atomicAdd(counter, 1u);
   old = __shfl(old, 0, 64);
-  const bool last = (old == expected - 1);
-  if (last) __threadfence();  // acquire the other splits' partials
-  return last;
+  return old == expected - 1;
 }
 
 // ---------------------------------------------------------- decode (a3, a4)
@@ -216,36 +263,16 @@ DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S) {
 // partials of (r, g) in split order and restores the counter to zero.
 template <class E, int D, int G>
 DEV void decode_finish(const PodParams& p, int r, int s, int S, int unit, int g) {
-  const int lane = lane_id();
   const int hkv = p.hkv;
   uint32_t* cnt = p.d_cnt + (int64_t)r * hkv + g;
   if (!arrive_last(cnt, (uint32_t)S)) return;
-
-  // last split merges all S partials of (r, g) in split order
-  const int unit0 = unit - s;
-  constexpr int MPL = D / 64;
-  for (int h = 0; h < G; ++h) {
-    float M = kNegInf;
-    for (int ss = 0; ss < S; ++ss) {
-      const float* ps = p.d_part + ((int64_t)(unit0 + ss) * hkv + g) * G * (D + 2);
-      M = fmaxf(M, ps[G * D + h]);
-    }
-    const float Mu = safe_max(M);
-    float a[MPL] = {};
-    float Lsum = 0.0f;
-    for (int ss = 0; ss < S; ++ss) {
-      const float* ps = p.d_part + ((int64_t)(unit0 + ss) * hkv + g) * G * (D + 2);
-      const float w = fast_exp2(ps[G * D + h] - Mu);
-      Lsum += w * ps[G * D + G + h];
-#pragma unroll
-      for (int e = 0; e < MPL; ++e) a[e] += w * ps[h * D + lane * MPL + e];
-    }
-    const float inv = 1.0f / Lsum;
-    const int64_t o = ((int64_t)r * p.hq + (int64_t)g * G + h) * D + lane * MPL;
-#pragma unroll
-    for (int e = 0; e < MPL; ++e) store_out<E>(p.od, o + e, a[e] * inv);
-  }
-  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // splits of (r, g) are wave tasks (unit - s + s') * hkv + g
+  const float* part0 = p.d_part + ((int64_t)(unit - s) * hkv + g) * G * (D + 2);
+  const int64_t sstride = (int64_t)hkv * G * (D + 2);
+  for (int h = 0; h < G; ++h)
+    merge_partials<E, D>(part0 + h * D, sstride, G * D - h * D + h, G * D + G - h * D + h, S, p.od,
+                         ((int64_t)r * p.hq + (int64_t)g * G + h) * D);
+  if (lane_id() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class E, int D, int G, int PF>
@@ -402,10 +429,10 @@ DEV void decode_wave(const PodParams& p, int wt) {
   for (int h = 0; h < G; ++h) {
     if ((h & 3) == slot) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) part[h * D + j * EPL + e] = acc[h][e];
+      for (int e = 0; e < EPL; ++e) st_dev(part + h * D + j * EPL + e, acc[h][e]);
       if (j == 0) {
-        part[G * D + h] = m[h];
-        part[G * D + G + h] = l[h];
+        st_dev(part + G * D + h, m[h]);
+        st_dev(part + G * D + G + h, l[h]);
       }
     }
   }
@@ -610,10 +637,10 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   if (h < G) {
 #pragma unroll
     for (int b = 0; b < DB; ++b)
-      *reinterpret_cast<float4*>(part + h * D + 16 * b + 4 * hq4) = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+      st_dev4(part + h * D + 16 * b + 4 * hq4, acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
     if (hq4 == 0) {
-      part[G * D + h] = m;
-      part[G * D + G + h] = l;
+      st_dev(part + G * D + h, m);
+      st_dev(part + G * D + G + h, l);
     }
   }
   decode_finish<Bf16, D, G>(p, r, s, S, unit, g);
@@ -750,28 +777,26 @@ DEV void stage_store_bf16(char* st, const uint4 (&kreg)[PfBf16<D>::KLOADS], cons
   }
 }
 
-// Tile-level arrival and merge, shared by both prefill flavours.
+// Tile-level arrival and merge, shared by both prefill flavours: every
+// thread waits for its own partial stores, the workgroup synchronises, one
+// thread counts the arrival, and the last split's workgroup merges.
 template <class E, int D, int RPW>
 DEV void prefill_finish_split(const PodParams& p, const TaskGeom& t, int task, int* flag) {
+  wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t old = atomicAdd(p.p_cnt + t.tile, 1u);
-    *flag = (old == (uint32_t)p.splits - 1u);
-  }
+  if (threadIdx.x == 0) *flag = atomicAdd(p.p_cnt + t.tile, 1u) == (uint32_t)p.splits - 1u;
   __syncthreads();
   if (!*flag) return;
-  __threadfence();
   const int w = wave_id();
   const int64_t rowheads = (int64_t)RPW * kWavesPerWG;
   // Tasks of one tile differ only in their split: task = split * tiles + (tile
   // position), so split s of this tile is task - (split - s) * tiles.
+  const int64_t sstride = (int64_t)p.tiles * rowheads * (D + 2);
   for (int rr = 0; rr < RPW; ++rr) {
     const int row = t.row0 + rr;
     if (row >= p.C) break;
-    const int64_t first = ((int64_t)(task - t.split * p.tiles) * rowheads + w * RPW + rr) * (D + 2);
-    const int64_t sstride = (int64_t)p.tiles * rowheads * (D + 2);
-    merge_row<E, D>(p.p_part + first, sstride, p.splits, p.op, ((int64_t)row * p.hq + t.head) * D);
+    const float* first = p.p_part + ((int64_t)(task - t.split * p.tiles) * rowheads + w * RPW + rr) * (D + 2);
+    merge_partials<E, D>(first, sstride, D, D + 1, p.splits, p.op, ((int64_t)row * p.hq + t.head) * D);
   }
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(p.p_cnt + t.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -926,11 +951,10 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, char* smem, int* flag) 
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq)
-      *reinterpret_cast<float4*>(pr + 32 * db + 8 * jq + 4 * half) =
-          make_float4(o[db][4 * jq], o[db][4 * jq + 1], o[db][4 * jq + 2], o[db][4 * jq + 3]);
+      st_dev4(pr + 32 * db + 8 * jq + 4 * half, o[db][4 * jq], o[db][4 * jq + 1], o[db][4 * jq + 2], o[db][4 * jq + 3]);
   if (half == 0) {
-    pr[D] = m;
-    pr[D + 1] = ltot;
+    st_dev(pr + D, m);
+    st_dev(pr + D + 1, ltot);
   }
   prefill_finish_split<Bf16, D, C::RPW>(p, t, task, flag);
 }
@@ -1037,9 +1061,9 @@ DEV void prefill_tile_f32(const PodParams& p, int task, char* smem, int* flag) {
   const int64_t rowheads = (int64_t)C::RPW * kWavesPerWG;
   float* pr = p.p_part + ((int64_t)task * rowheads + wave_id() * C::RPW + lane) * (D + 2);
 #pragma unroll
-  for (int e = 0; e < D; e += 4) *reinterpret_cast<float4*>(pr + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-  pr[D] = m;
-  pr[D + 1] = l;
+  for (int e = 0; e < D; e += 4) st_dev4(pr + e, acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  st_dev(pr + D, m);
+  st_dev(pr + D + 1, l);
   prefill_finish_split<F32, D, C::RPW>(p, t, task, flag);
 }
 
@@ -1111,11 +1135,15 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
         x = atomicAdd(p.ctrl + role, 1u);
       }
       task = (int)x;
-      const uint32_t done = __hip_atomic_fetch_add(p.ctrl + 2, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (done == (uint32_t)p.grid - 1u) {  // every workgroup has claimed: reset the queues
+      // The claim has been performed (its value returned) before the claim
+      // count is bumped, so the workgroup that sees every claim counted can
+      // reset the queue heads for the next launch.
+      wait_vmem();
+      const uint32_t done = atomicAdd(p.ctrl + 2, 1u);
+      if (done == (uint32_t)p.grid - 1u) {
         __hip_atomic_store(p.ctrl + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(p.ctrl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.ctrl + 2, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctrl + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     role_task[0] = role;
