@@ -41,6 +41,15 @@ struct F32 {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// The LDS a workgroup works in: four separately declared stage buffers (so
+// the compiler can tell which one an LDS-DMA load writes and never has to
+// wait for all of them before an LDS read) and the split's page ids.
+struct LdsBufs {
+  char* st[4];
+  int* pids;
+  int* flag;
+};
+
 // ------------------------------------------------------------------ helpers
 DEV float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 DEV float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -647,11 +656,15 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
 }
 
 template <class E, int D, int G, int PF>
-DEV void decode_wg(const PodParams& p, int wg_task, char* smem) {
+DEV void decode_wg(const PodParams& p, int wg_task, const LdsBufs& lb) {
   const int wt = wg_task * kWavesPerWG + wave_id();
   if (wt >= p.d_wave_tasks) return;
   if constexpr (E::bytes == 2)
-    decode_wave_mfma<D, G>(p, wt, smem + wave_id() * DecMfma<D>::LDS_WAVE);
+  {
+    const int w = wave_id();
+    char* buf = w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3];
+    decode_wave_mfma<D, G>(p, wt, buf);
+  }
   else
     decode_wave<E, D, G, PF>(p, wt);
 }
@@ -692,88 +705,70 @@ DEV TaskGeom prefill_geom(const PodParams& p, int task) {
   return t;
 }
 
-// bf16 prefill tile: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16.
-// Lane l owns query row (l & 31) of its wave; its half h = l >> 5 owns half of
-// every 32-key score column, so row max and row sum are mostly in-lane.
-template <int D>
-struct PfBf16 {
-  static constexpr int RPW = 32;
-  static constexpr int BN = 64;                       // keys per staged block
-  static constexpr int KSTR = (D + 8) * 2;            // K row stride (bytes), padded
-  static constexpr int VSTR = (BN + 8) * 2;           // V^T row stride (bytes), padded
-  static constexpr int KBYTES = BN * KSTR;
-  static constexpr int STAGE = KBYTES + D * VSTR;
-  static constexpr int PIDS = kMaxSplitKeys / kPageSize;   // page ids of one split
-  static constexpr int LDS = 2 * STAGE + PIDS * 4;
-  static constexpr int CH = D / 8;                    // 16-byte chunks per key row
-  static constexpr int KLOADS = CH / 4;               // K chunks per thread per block
-};
-
-// Position of key k (0..63) inside a V^T row: bits 2 and 3 swapped, so that
-// the 8 keys one MFMA lane feeds for P^T are contiguous (see prefill_tile).
-DEV int vt_pos(int k) { return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
-
 // Copy the physical ids of pages [pg0, pg0 + n) into LDS (clamped into the pool).
 DEV void preload_page_ids(const PodParams& p, int pg0, int n, int* pids) {
   for (int i = threadIdx.x; i < n; i += 256) pids[i] = (int)min((uint32_t)p.pt_p[pg0 + i], p.num_pages - 1u);
 }
 
-template <int D>
-DEV void stage_load_bf16(const PodParams& p, const int* pids, int pg0, int kb0, uint4 (&kreg)[PfBf16<D>::KLOADS], uint4 (&vreg)[4]) {
-  using C = PfBf16<D>;
-  const int tid = threadIdx.x;
-  const int64_t tok_bytes = (int64_t)p.hkv * D * 2;
-#pragma unroll
-  for (int i = 0; i < C::KLOADS; ++i) {
-    const int idx = tid + 256 * i;
-    const int key = kb0 + idx / C::CH;
-    const int c = idx % C::CH;
-    kreg[i] = make_uint4(0, 0, 0, 0);
-    if (key < p.Lp) {
-      const int64_t page = pids[(key >> 4) - pg0];
-      const char* src = reinterpret_cast<const char*>(p.k_pool) + (page * kPageSize + (key & 15)) * tok_bytes + c * 16;
-      kreg[i] = *reinterpret_cast<const uint4*>(src);
-    }
-  }
-  if (tid < 16 * C::CH) {
-    const int c = tid >> 4, kq = tid & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb0 + 4 * kq + i;
-      vreg[i] = make_uint4(0, 0, 0, 0);
-      if (key < p.Lp) {
-        const int64_t page = pids[(key >> 4) - pg0];
-        const char* src = reinterpret_cast<const char*>(p.v_pool) + (page * kPageSize + (key & 15)) * tok_bytes + c * 16;
-        vreg[i] = *reinterpret_cast<const uint4*>(src);
-      }
-    }
-  }
+// Wait until at most N of this wave's vector memory operations are in flight
+// and all its LDS operations are done (s_waitcnt vmcnt(N) lgkmcnt(0)).
+template <int N>
+DEV void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// bf16 prefill tile: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16.
+// Lane l owns query row (l & 31) of its wave; its half h = l >> 5 owns half of
+// every 32-key score column, so row max and row sum are mostly in-lane.
+//
+// K/V blocks of 32 keys stream from the paged pool straight into LDS
+// (global_load_lds_dwordx4, no register staging) through NS stages, NS - 1
+// blocks ahead of the block being computed.  Rows are stored unpadded; the
+// 16-byte chunks of each row are XOR-swizzled on the global side so that the
+// MFMA operand reads hit distinct LDS banks: K row r keeps chunk c at
+// c ^ (r & 7) (read 32 rows x 16 bytes with ds_read_b128), V row r at
+// c ^ 2(r & 3) (read 4 rows x 32 bytes per 16 lanes with the transposing
+// ds_read_b64_tr_b16, which hands each lane one d-column of 4 keys).
 template <int D>
-DEV void stage_store_bf16(char* st, const uint4 (&kreg)[PfBf16<D>::KLOADS], const uint4 (&vreg)[4]) {
+struct PfBf16 {
+  static constexpr int RPW = 32;                 // query rows per wave
+  static constexpr int BN = 32;                  // keys per staged block
+  static constexpr int NS = 4;                   // LDS stages
+  static constexpr int ROWB = D * 2;             // bytes per key row
+  static constexpr int OPB = BN * ROWB;          // bytes per operand per stage
+  static constexpr int STAGE = 2 * OPB;          // K block then V block
+  static constexpr int CH = D / 8;               // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;            // rows per 64-lane DMA instruction
+  static constexpr int IPW = BN / RPI / kWavesPerWG;  // DMA instructions per operand per wave
+  static constexpr int LPB = 2 * IPW;            // DMA loads per wave per block
+  static constexpr int PIDS = kMaxSplitKeys / kPageSize;
+  static constexpr int LDS = NS * STAGE + PIDS * 4;
+  static_assert(IPW >= 1, "block too small for the workgroup");
+};
+
+template <int D>
+DEV void prefill_issue_block(const char* kpool, const char* vpool, int64_t tok_bytes, const int* pids, int pg0,
+                             int Lp, int kb0, char* stage) {
   using C = PfBf16<D>;
-  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int pos = lane % C::CH;
 #pragma unroll
-  for (int i = 0; i < C::KLOADS; ++i) {
-    const int idx = tid + 256 * i;
-    *reinterpret_cast<uint4*>(st + (idx / C::CH) * C::KSTR + (idx % C::CH) * 16) = kreg[i];
-  }
-  if (tid < 16 * C::CH) {
-    const int c = tid >> 4, kq = tid & 15;
-    char* vt = st + C::KBYTES + vt_pos(4 * kq) * 2;
-    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-    const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-    const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      uint2 w;
-      w.x = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], sel);
-      w.y = __builtin_amdgcn_perm(v3[e >> 1], v2[e >> 1], sel);
-      *reinterpret_cast<uint2*>(vt + (8 * c + e) * C::VSTR) = w;
-    }
+  for (int i = 0; i < C::IPW; ++i) {
+    const int ins = wave_id() * C::IPW + i;
+    const int row = ins * C::RPI + lane / C::CH;
+    const int key = min(kb0 + row, Lp - 1);  // rows past the request re-read a valid key; masked later
+    const int64_t base = ((int64_t)pids[(key >> 4) - pg0] * kPageSize + (key & 15)) * tok_bytes;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(kpool + base + ((pos ^ (row & 7)) << 4)),
+                                     (lds_void_t*)(stage + ins * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(vpool + base + ((pos ^ (2 * (row & 3))) << 4)),
+                                     (lds_void_t*)(stage + C::OPB + ins * 1024), 16, 0, 0);
   }
 }
 
@@ -803,19 +798,18 @@ DEV void prefill_finish_split(const PodParams& p, const TaskGeom& t, int task, i
 }
 
 template <int D>
-DEV void prefill_tile_bf16(const PodParams& p, int task, char* smem, int* flag) {
+DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
   using C = PfBf16<D>;
+  static_assert(C::NS == 4, "the block loop is unrolled over four stage buffers");
   constexpr int KS = D / 16;   // MFMA k-steps over d
   constexpr int DB = D / 32;   // 32-wide d blocks of O^T
   const TaskGeom t = prefill_geom<C::RPW>(p, task);
   const int lane = lane_id();
   const int half = lane >> 5, rl = lane & 31;
   const int row = t.row0 + rl;
-
-  // kv-head offset folded into the pool pointers
-  PodParams pk = p;
-  pk.k_pool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)t.g * D * 2;
-  pk.v_pool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)t.g * D * 2;
+  const int64_t tok_bytes = (int64_t)p.hkv * D * 2;
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)t.g * D * 2;
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)t.g * D * 2;
 
   // Q^T operand: lane holds d = 16 ks + 8 half .. +8 of its row
   bf16x8_t qf[KS];
@@ -839,93 +833,108 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, char* smem, int* flag) 
   const int nblk = t.k1 > t.k0 ? (t.k1 - t.k0 + C::BN - 1) / C::BN : 0;
   const int lim = p.P0 + row;  // last visible key of this lane's row
 
-  // page ids of every block of this split (keys past Lp are never loaded)
-  int* pids = reinterpret_cast<int*>(smem + 2 * C::STAGE);
+  int* pids = lb.pids;
   const int pg0 = t.k0 / kPageSize;
-  const int pg1 = min((p.Lp + kPageSize - 1) / kPageSize, (t.k0 + nblk * C::BN) / kPageSize);
+  const int pg1 = min((p.Lp + kPageSize - 1) / kPageSize, (t.k0 + nblk * C::BN + kPageSize - 1) / kPageSize);
   preload_page_ids(p, pg0, pg1 - pg0, pids);
   __syncthreads();
 
-  uint4 kreg[C::KLOADS], vreg[4];
   if (nblk > 0) {
-    stage_load_bf16<D>(pk, pids, pg0, t.k0, kreg, vreg);
-    stage_store_bf16<D>(smem, kreg, vreg);
-  }
-  __syncthreads();
-  for (int b = 0; b < nblk; ++b) {
-    const int kb0 = t.k0 + b * C::BN;
-    char* st = smem + (b & 1) * C::STAGE;
-    if (b + 1 < nblk) stage_load_bf16<D>(pk, pids, pg0, kb0 + C::BN, kreg, vreg);
-    if (kb0 < t.kw) {
-      // ---- scores S^T (keys x rows), two 32-key tiles
-      f32x16_t sc[2];
+    // prologue: blocks 0 .. NS-2 (past the last block, the last block again)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+    for (int s = 0; s < C::NS - 1; ++s)
+      prefill_issue_block<D>(kpool, vpool, tok_bytes, pids, pg0, p.Lp, t.k0 + min(s, nblk - 1) * C::BN, lb.st[s]);
+    // per-lane LDS byte offsets of the MFMA operands inside a stage
+    const int krow_off = rl * C::ROWB;
+    const int ksw = rl & 7;
+    const int gq = lane >> 4, ti = lane & 15;
+    const int th = gq >> 1, tdh = gq & 1, tk = ti >> 2, tj = ti & 3;
+    // The loop runs a multiple of NS blocks with the same DMA and barrier
+    // sequence in every step (steps past nblk only re-load the last block), so
+    // the compiler sees one straight-line wait pattern per stage buffer.
+    for (int b0 = 0; b0 < nblk; b0 += C::NS) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sc[tt][j] = 0.0f;
-        const char* kr = st + (32 * tt + rl) * C::KSTR + 16 * half;
+    for (int u = 0; u < C::NS; ++u) {
+      const int b = b0 + u;
+      // this wave's loads of block b are done once at most NS-2 newer blocks remain in flight
+      wait_vm_lgkm<C::LPB * (C::NS - 2)>();
+      __builtin_amdgcn_s_barrier();
+      prefill_issue_block<D>(kpool, vpool, tok_bytes, pids, pg0, p.Lp,
+                             t.k0 + min(b + C::NS - 1, nblk - 1) * C::BN, lb.st[(u + C::NS - 1) % C::NS]);
+      const int kb0 = t.k0 + b * C::BN;
+      if (b >= nblk || kb0 >= t.kw) continue;
+      const char* st = lb.st[u];
+      // ---- scores S^T (32 keys x 32 rows)
+      f32x16_t sc;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
-          sc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[tt], 0, 0, 0);
-        }
+      for (int j = 0; j < 16; ++j) sc[j] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + krow_off + (((2 * ks + half) ^ ksw) << 4));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc, 0, 0, 0);
       }
-      // ---- scale, causal mask, online softmax (base 2)
+      // ---- scale, causal mask, online softmax (base 2; the max is raised
+      //      only when a score exceeds it by more than 8)
       const bool need_mask = (kb0 + C::BN - 1) > (p.P0 + t.row0);
       float mx = kNegInf;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float s = sc[tt][j] * p.scale_log2;
-          if (need_mask) {
-            const int key = kb0 + 32 * tt + 8 * (j >> 2) + 4 * half + (j & 3);
-            s = key <= lim ? s : kNegInf;
-          }
-          sc[tt][j] = s;
-          mx = fmaxf(mx, s);
+      for (int j = 0; j < 16; ++j) {
+        float s = sc[j] * p.scale_log2;
+        if (need_mask) {
+          const int key = kb0 + 8 * (j >> 2) + 4 * half + (j & 3);
+          s = key <= lim ? s : kNegInf;
         }
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      const float mu = safe_max(mnew);
-      const float alpha = fast_exp2(m - mu);
-      float ps = 0.0f;
-      bf16x8_t pf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const float e0 = fast_exp2(sc[ks >> 1][8 * (ks & 1) + 2 * q2] - mu);
-          const float e1 = fast_exp2(sc[ks >> 1][8 * (ks & 1) + 2 * q2 + 1] - mu);
-          ps += e0 + e1;
-          w4[q2] = pack_bf16(e0, e1);
-        }
-        pf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        sc[j] = s;
+        mx = fmaxf(mx, s);
       }
-      l = l * alpha + ps;
-      m = mnew;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      mx = fmaxf(mx, xor_lane(mx, 32));
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - safe_max(mnew));
+        l *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        m = mnew;
       }
-      // ---- O^T += V^T P^T
-      const char* vt = st + C::KBYTES;
+      const float mu = safe_max(m);
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const float e0 = fast_exp2(sc[8 * ks + 2 * q2] - mu);
+          const float e1 = fast_exp2(sc[8 * ks + 2 * q2 + 1] - mu);
+          l += e0 + e1;
+          w4[q2] = pack_bf16(e0, e1);
+        }
+        pf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+      }
+      // ---- O^T += V^T P^T: keys 16ks + 4th + tk (first read) and +8 (second)
+      const char* vt = st + C::OPB;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char* vr = vt + (32 * db + rl) * C::VSTR + 16 * half;
+        const int c = 4 * db + 2 * tdh + (tj >> 1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vr + ks * 32);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int r0 = 16 * ks + 4 * th + tk, r1 = r0 + 8;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vt + r0 * C::ROWB + ((c ^ (2 * (r0 & 3))) << 4) + ((tj & 1) << 3)));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vt + r1 * C::ROWB + ((c ^ (2 * (r1 & 3))) << 4) + ((tj & 1) << 3)));
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (short __attribute__((ext_vector_type(8)))){
+              lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
         }
       }
     }
-    if (b + 1 < nblk) stage_store_bf16<D>(smem + ((b + 1) & 1) * C::STAGE, kreg, vreg);
-    __syncthreads();
+    }
+
+    wait_vmem();  // no DMA may still target this workgroup's LDS when it is reused
   }
+  __syncthreads();
 
   const float ltot = l + xor_lane(l, 32);
   if (p.splits == 1) {
@@ -956,7 +965,7 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, char* smem, int* flag) 
     st_dev(pr + D, m);
     st_dev(pr + D + 1, ltot);
   }
-  prefill_finish_split<Bf16, D, C::RPW>(p, t, task, flag);
+  prefill_finish_split<Bf16, D, C::RPW>(p, t, task, lb.flag);
 }
 
 // fp32 prefill tile (exact fp32, VALU): lane = one query row, K/V blocks of 32
@@ -965,17 +974,17 @@ template <int D>
 struct PfF32 {
   static constexpr int RPW = 64;
   static constexpr int BN = 32;
-  static constexpr int LDS = 2 * BN * D * 4;
+  static constexpr int STAGE = BN * D * 4;  // one operand block per stage buffer
 };
 
 template <int D>
-DEV void prefill_tile_f32(const PodParams& p, int task, char* smem, int* flag) {
+DEV void prefill_tile_f32(const PodParams& p, int task, const LdsBufs& lb) {
   using C = PfF32<D>;
   const TaskGeom t = prefill_geom<C::RPW>(p, task);
   const int lane = lane_id();
   const int row = t.row0 + lane;
-  float* ks = reinterpret_cast<float*>(smem);
-  float* vs = ks + C::BN * D;
+  float* ks = reinterpret_cast<float*>(lb.st[0]);
+  float* vs = reinterpret_cast<float*>(lb.st[1]);
 
   float q[D], acc[D];
   {
@@ -1064,21 +1073,36 @@ DEV void prefill_tile_f32(const PodParams& p, int task, char* smem, int* flag) {
   for (int e = 0; e < D; e += 4) st_dev4(pr + e, acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
   st_dev(pr + D, m);
   st_dev(pr + D + 1, l);
-  prefill_finish_split<F32, D, C::RPW>(p, t, task, flag);
+  prefill_finish_split<F32, D, C::RPW>(p, t, task, lb.flag);
 }
 
 template <class E, int D>
 struct PfSel;
 template <int D>
 struct PfSel<Bf16, D> {
-  static constexpr int LDS = PfBf16<D>::LDS;
-  static DEV void run(const PodParams& p, int task, char* smem, int* flag) { prefill_tile_bf16<D>(p, task, smem, flag); }
+  static constexpr int STAGE = PfBf16<D>::STAGE;
+  static DEV void run(const PodParams& p, int task, const LdsBufs& lb) { prefill_tile_bf16<D>(p, task, lb); }
 };
 template <int D>
 struct PfSel<F32, D> {
-  static constexpr int LDS = PfF32<D>::LDS;
-  static DEV void run(const PodParams& p, int task, char* smem, int* flag) { prefill_tile_f32<D>(p, task, smem, flag); }
+  static constexpr int STAGE = PfF32<D>::STAGE;
+  static DEV void run(const PodParams& p, int task, const LdsBufs& lb) { prefill_tile_f32<D>(p, task, lb); }
 };
+
+// Stage buffer size: large enough for a prefill stage and a decode wave's V pages.
+template <class E, int D>
+constexpr int stage_bytes() {
+  return PfSel<E, D>::STAGE > DecMfma<D>::LDS_WAVE ? PfSel<E, D>::STAGE : DecMfma<D>::LDS_WAVE;
+}
+
+#define POD_DECLARE_LDS(E, D)                                                          \
+  __shared__ __attribute__((aligned(16))) char lds_st0[stage_bytes<E, D>()];             \
+  __shared__ __attribute__((aligned(16))) char lds_st1[stage_bytes<E, D>()];             \
+  __shared__ __attribute__((aligned(16))) char lds_st2[stage_bytes<E, D>()];             \
+  __shared__ __attribute__((aligned(16))) char lds_st3[stage_bytes<E, D>()];             \
+  __shared__ int lds_pids[kMaxSplitKeys / kPageSize];                                    \
+  __shared__ int lds_flag;                                                               \
+  const LdsBufs lb{{lds_st0, lds_st1, lds_st2, lds_st3}, lds_pids, &lds_flag}
 
 // ------------------------------------------------------------------ kernels
 // Pages in flight per decode wave: the fused kernel keeps 2 WGs per CU, so its
@@ -1092,18 +1116,19 @@ constexpr int decode_min_blocks() { return E::bytes == 2 ? 2 : (G >= 4 ? 2 : 4);
 
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(PodParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[PfSel<E, D>::LDS];
-  __shared__ int flag;
-  PfSel<E, D>::run(p, blockIdx.x, smem, &flag);
+  POD_DECLARE_LDS(E, D);
+  PfSel<E, D>::run(p, blockIdx.x, lb);
 }
-
-template <class E, int D>
-constexpr int decode_lds() { return E::bytes == 2 ? kWavesPerWG * DecMfma<D>::LDS_WAVE : 16; }
 
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, (decode_min_blocks<E, G>())) void pod_decode_kernel(PodParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[decode_lds<E, D>()];
-  decode_wg<E, D, G, decode_pf<E>()>(p, blockIdx.x, smem);
+  constexpr int W = E::bytes == 2 ? DecMfma<D>::LDS_WAVE : 16;  // one V buffer per wave
+  __shared__ __attribute__((aligned(16))) char dbuf0[W];
+  __shared__ __attribute__((aligned(16))) char dbuf1[W];
+  __shared__ __attribute__((aligned(16))) char dbuf2[W];
+  __shared__ __attribute__((aligned(16))) char dbuf3[W];
+  const LdsBufs lb{{dbuf0, dbuf1, dbuf2, dbuf3}, nullptr, nullptr};
+  decode_wg<E, D, G, decode_pf<E>()>(p, blockIdx.x, lb);
 }
 
 // Fused hybrid kernel.  Each workgroup takes a ticket on its CU's counter;
@@ -1115,9 +1140,8 @@ __global__ __launch_bounds__(256, (decode_min_blocks<E, G>())) void pod_decode_k
 // exactly once, with no workgroup ever waiting for another.
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[PfSel<E, D>::LDS];
+  POD_DECLARE_LDS(E, D);
   __shared__ int role_task[2];
-  __shared__ int flag;
   if (threadIdx.x == 0) {
     int role, task;
     if (p.policy == kPolicyStatic) {
@@ -1152,9 +1176,9 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   __syncthreads();
   const int role = role_task[0], task = role_task[1];
   if (role == 0) {
-    if (task < p.p_tasks) PfSel<E, D>::run(p, task, smem, &flag);
+    if (task < p.p_tasks) PfSel<E, D>::run(p, task, lb);
   } else {
-    if (task < p.d_wg_tasks) decode_wg<E, D, G, fused_pf<E, G>()>(p, task, smem);
+    if (task < p.d_wg_tasks) decode_wg<E, D, G, fused_pf<E, G>()>(p, task, lb);
   }
 }
 
