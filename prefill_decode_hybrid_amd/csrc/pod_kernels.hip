@@ -450,24 +450,32 @@ DEV void decode_wave(const PodParams& p, int wt) {
 
 // bf16 decode on MFMA (v_mfma_f32_16x16x32_bf16), 16 query-head columns of
 // which the G heads of kv head g are used.  Per pair of pages (32 keys):
-//   S^T[key, head] = K Q^T     A = K rows straight from HBM (lane: key l%16,
-//                              8 d-elements at 8*(l/16) of each 32-d chunk),
-//                              B = Q^T held in registers;
-//   O^T[d, head] += V^T P^T    A = V^T read from this wave's LDS copy of the
-//                              two V pages with ds_read_b64_tr_b16 (the
+//   S^T[key, head] = K Q^T     A = K rows (lane: key l%16, 8 d-elements at
+//                              8*(l/16) of each 32-d chunk), B = Q^T in
+//                              registers;
+//   O^T[d, head] += V^T P^T    A = V^T via ds_read_b64_tr_b16 (the
 //                              transposing LDS read), B = P^T straight from
 //                              the S^T accumulators.
+// K and V leave HBM in whole 256-byte head rows (16 lanes per token, four
+// tokens per load, nontemporal), which streams far better than the 64-byte
+// pieces the MFMA operand layout would ask for, and pass through this wave's
+// own LDS buffer (no barrier: the buffer is private to the wave).  Row chunks
+// are XOR-swizzled in LDS so the operand reads are free of bank conflicts.
 // The key order inside an MFMA step is permuted identically on both sides
-// (lane quad q feeds keys 4q..4q+3 of each page), so no data is reshuffled.
-// The softmax maximum is raised only when a score exceeds it by more than
-// 2^8 (base-2 units of 8); exp2(s - m) <= 256 then, and the final division
-// by l is unchanged, so the result is the same exact softmax.
+// (lane quad q feeds keys 4q..4q+3 of each page), so nothing is reshuffled.
+// The softmax maximum is raised only when a score exceeds it by more than 8
+// (base 2), so exp2(s - m) <= 256; the final division by l is unchanged, so
+// the result is the same exact softmax.
 template <int D>
 struct DecMfma {
   static constexpr int KC = D / 32;          // QK k-chunks
   static constexpr int DB = D / 16;          // PV d-blocks
-  static constexpr int VROW = D * 2 + 32;    // LDS row stride (bytes), padded
-  static constexpr int LDS_WAVE = 32 * VROW; // two pages of V per wave
+  static constexpr int ROWB = D * 2;         // bytes per token row of one head
+  static constexpr int CHR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CHR;       // rows per load instruction
+  static constexpr int NI = 16 / RPI;        // load instructions per page per operand
+  static constexpr int OPB = 32 * ROWB;      // LDS bytes per operand (two pages)
+  static constexpr int LDS_WAVE = 2 * OPB;   // K pages then V pages
   static constexpr float kLazy = 8.0f;
 };
 
@@ -476,11 +484,13 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+DEV int ksw(int row) { return row & 7; }        // K chunk swizzle (ds_read_b128 over 8 rows)
+DEV int vsw(int row) { return 2 * (row & 3); }  // V chunk swizzle (transposing reads, 4 rows)
 
 template <int D, int G>
 DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   using C = DecMfma<D>;
-  constexpr int KC = C::KC, DB = C::DB;
+  constexpr int KC = C::KC, DB = C::DB, NI = C::NI;
   const int lane = lane_id();
   const int hkv = p.hkv;
   const int g = wt % hkv;
@@ -495,17 +505,18 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   const int t1 = min(t0 + p.T, L);
   const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
   const int npair = (npg + 1) >> 1;
-  const int kk = lane & 15, dq = lane >> 4;   // load role: key in page, 8-element quarter
+  const int kk = lane & 15, q4 = lane >> 4;       // MFMA roles: key / head column, quad
+  const int lrow = lane / C::CHR, lchk = lane % C::CHR;  // load role: row in group, chunk
 
   int pid = 0;
   if (lane < npg) pid = p.pt_d[(int64_t)r * p.stride + t0 / kPageSize + lane];
   pid = (int)min((uint32_t)pid, p.num_pages - 1u);
 
-  // Q^T operand: column = head kk (< G), rows d = 32c + 8dq .. +8
+  // Q^T operand: column = head kk (< G), rows d = 32c + 8q4 .. +8
   bf16x8_t qf[KC];
   {
     const char* qb = reinterpret_cast<const char*>(p.qd) +
-                     (((int64_t)r * p.hq + (int64_t)g * G + kk) * D + 8 * dq) * 2;
+                     (((int64_t)r * p.hq + (int64_t)g * G + kk) * D + 8 * q4) * 2;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -515,57 +526,65 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   }
   const int64_t tok_bytes = (int64_t)hkv * D * 2;
   const int64_t page_bytes = kPageSize * tok_bytes;
-  const int64_t lane_off = (int64_t)kk * tok_bytes + ((int64_t)g * D + 8 * dq) * 2;
+  const int64_t lane_off = (int64_t)lrow * tok_bytes + (int64_t)g * C::ROWB + lchk * 16;
   const char* kb = reinterpret_cast<const char*>(p.k_pool) + lane_off;
   const char* vb = reinterpret_cast<const char*>(p.v_pool) + lane_off;
+  char* kl = lds;            // K rows of the pair
+  char* vl = lds + C::OPB;   // V rows of the pair
 
   f32x4_t acc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, l = 0.0f;
 
-  u32x4_t kr[2][2][KC], vr[2][2][KC];
-  auto issue = [&](u32x4_t (&kd)[2][KC], u32x4_t (&vd)[2][KC], int pair) __attribute__((always_inline)) {
-    // A missing second page (odd page count) re-reads the last page; every key
-    // past t1 is masked in consume(), so its values never reach the result.
+  u32x4_t kr[2][2][NI], vr[2][2][NI];
+  // A missing second page (odd page count) re-reads the last page; every key
+  // past t1 is masked in consume(), so its values never reach the result.
+  auto issue = [&](u32x4_t (&kd)[2][NI], u32x4_t (&vd)[2][NI], int pair) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       const int pg = min(2 * pair + pp, npg - 1);
       const int64_t off = (int64_t)__builtin_amdgcn_readlane(pid, pg) * page_bytes;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kd[pp][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + off + c * 64));
+      for (int u = 0; u < NI; ++u)
+        kd[pp][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + off + u * C::RPI * tok_bytes));
 #pragma unroll
-      for (int c = 0; c < KC; ++c) vd[pp][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + off + c * 64));
+      for (int u = 0; u < NI; ++u)
+        vd[pp][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + off + u * C::RPI * tok_bytes));
     }
   };
 
-  const int hq4 = lane >> 4;  // MFMA output role: keys 4*hq4 .. +4 of each page
-  auto consume = [&](const u32x4_t (&kd)[2][KC], const u32x4_t (&vd)[2][KC], int pair) __attribute__((always_inline)) {
+  auto consume = [&](const u32x4_t (&kd)[2][NI], const u32x4_t (&vd)[2][NI], int pair) __attribute__((always_inline)) {
     const int kbase = t0 + 32 * pair;
-    // V pages -> LDS (rows = keys), invisible keys zeroed
+    // K and V rows of the pair -> LDS (invisible V rows zeroed)
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const bool ok = kbase + 16 * pp + kk < t1;
+    for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        *reinterpret_cast<u32x4_t*>(lds + (16 * pp + kk) * C::VROW + (32 * c + 8 * dq) * 2) =
-            ok ? vd[pp][c] : (u32x4_t){0u, 0u, 0u, 0u};
-    }
+      for (int u = 0; u < NI; ++u) {
+        const int row = 16 * pp + u * C::RPI + lrow;
+        const bool ok = kbase + row < t1;
+        *reinterpret_cast<u32x4_t*>(kl + row * C::ROWB + ((lchk ^ ksw(row)) << 4)) = kd[pp][u];
+        *reinterpret_cast<u32x4_t*>(vl + row * C::ROWB + ((lchk ^ vsw(row)) << 4)) =
+            ok ? vd[pp][u] : (u32x4_t){0u, 0u, 0u, 0u};
+      }
     // S^T for both pages
     f32x4_t sc[2];
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       sc[pp] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      const int row = 16 * pp + kk;
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        sc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kd[pp][c]), qf[c], sc[pp], 0, 0, 0);
+      for (int c = 0; c < KC; ++c) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + row * C::ROWB + (((4 * c + q4) ^ ksw(row)) << 4));
+        sc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], sc[pp], 0, 0, 0);
+      }
     }
     float mloc = kNegInf;
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = kbase + 16 * pp + 4 * hq4 + i < t1;
+        const bool ok = kbase + 16 * pp + 4 * q4 + i < t1;
         const float v = ok ? sc[pp][i] * p.scale_log2 : kNegInf;
         sc[pp][i] = v;
         mloc = fmaxf(mloc, v);
@@ -591,15 +610,17 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
       pw[2 * pp + 1] = pack_bf16(e2, e3);
     }
     const bf16x8_t pf = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-    // O^T += V^T P^T; lane (quad hq4, i = 4k + j) reads keys 4*hq4 + k, d = 16b + 4j .. +4
+    // O^T += V^T P^T; lane (quad q4, i = 4k + j) reads keys 4*q4 + k of each
+    // page, d = 16b + 4j .. +4
     const int tk = (lane & 15) >> 2, tj = lane & 3;
-    const char* tr0 = lds + (4 * hq4 + tk) * C::VROW + 4 * tj * 2;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t*)(tr0 + 32 * b));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t*)(tr0 + 16 * C::VROW + 32 * b));
+      const int chunk = 2 * b + (tj >> 1);
+      const int r0 = 4 * q4 + tk, r1 = 16 + r0;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(
+          vl + r0 * C::ROWB + ((chunk ^ vsw(r0)) << 4) + ((tj & 1) << 3)));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(
+          vl + r1 * C::ROWB + ((chunk ^ vsw(r1)) << 4) + ((tj & 1) << 3)));
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (short __attribute__((ext_vector_type(8)))){
           lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc[b], 0, 0, 0);
@@ -631,7 +652,7 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   if (S == 1) {
     if (h < G) {
       const float inv = 1.0f / l;
-      char* orow = reinterpret_cast<char*>(p.od) + (((int64_t)r * p.hq + (int64_t)g * G + h) * D + 4 * hq4) * 2;
+      char* orow = reinterpret_cast<char*>(p.od) + (((int64_t)r * p.hq + (int64_t)g * G + h) * D + 4 * q4) * 2;
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
         uint2 w;
@@ -645,9 +666,8 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   float* part = p.d_part + (int64_t)wt * G * (D + 2);
   if (h < G) {
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
-      st_dev4(part + h * D + 16 * b + 4 * hq4, acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
-    if (hq4 == 0) {
+    for (int b = 0; b < DB; ++b) st_dev4(part + h * D + 16 * b + 4 * q4, acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    if (q4 == 0) {
       st_dev(part + G * D + h, m);
       st_dev(part + G * D + G + h, l);
     }
