@@ -72,12 +72,17 @@ enum pod_status {
 
 enum pod_dtype { POD_BF16 = 0, POD_F32 = 1 };
 
-/* Role policy of the fused launch (paper §5.4.2 compares proportional and
- * 50:50 allocation; §3.3 studies CTA-parallel fusion without SM awareness). */
+/* Role policy of the fused launch.  The default follows the paper's
+ * SM-aware scheduling (§4.1): a workgroup looks at how many prefill and
+ * decode workgroups already run on its compute unit and takes the role that
+ * is short of its share.  The others are the paper's comparison points:
+ * proportional and 50:50 ticket sequences (§5.4.2) and a fixed split by
+ * workgroup id, i.e. CTA-parallel fusion without SM awareness (§3.3). */
 enum pod_policy {
-    POD_POLICY_PROPORTIONAL = 0, /* per-CU share of prefill = prefill tasks / all tasks */
-    POD_POLICY_HALF = 1,         /* alternate prefill and decode on every CU          */
-    POD_POLICY_STATIC = 2        /* workgroup id decides the role, no CU awareness     */
+    POD_POLICY_CU_BALANCED = 0,  /* per-CU running counts; prefill slots = plan share   */
+    POD_POLICY_PROPORTIONAL = 1, /* per-CU tickets, prefill share = prefill / all tasks */
+    POD_POLICY_HALF = 2,         /* per-CU tickets alternating prefill and decode       */
+    POD_POLICY_STATIC = 3        /* workgroup id decides the role, no CU awareness      */
 };
 
 typedef struct {
@@ -135,6 +140,7 @@ typedef struct {
     int32_t decode_wave_tasks;  /* (request, kv head, token split) units, one wave each */
     int32_t decode_wg_tasks;    /* decode workgroups (4 wave tasks each)               */
     int32_t share_num, share_den; /* prefill share of each CU's tickets               */
+    int32_t cu_prefill_slots;   /* CU-balanced policy: prefill workgroups kept per CU  */
     int32_t policy;
 } pod_attn_stats;
 

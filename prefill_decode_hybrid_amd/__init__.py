@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libpodattn.so")
 
 POD_OK, POD_ERR_INVALID_ARG, POD_ERR_UNSUPPORTED, POD_ERR_WORKSPACE, POD_ERR_HIP = 0, -1, -2, -3, -4
 POD_BF16, POD_F32 = 0, 1
-POD_POLICY_PROPORTIONAL, POD_POLICY_HALF, POD_POLICY_STATIC = 0, 1, 2
+POD_POLICY_CU_BALANCED, POD_POLICY_PROPORTIONAL, POD_POLICY_HALF, POD_POLICY_STATIC = 0, 1, 2, 3
 MODE_HYBRID, MODE_PREFILL, MODE_DECODE = 0, 1, 2
 
 EXPORTED = ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_prefill_only",
@@ -54,7 +54,7 @@ class PodAttnStats(ctypes.Structure):
         "mode", "fallback", "num_cus", "wg_per_cu", "grid", "prefill_rows_per_tile",
         "prefill_heads_per_tile", "prefill_tiles", "prefill_splits", "prefill_split_keys",
         "prefill_tasks", "decode_split_tokens", "decode_wave_tasks", "decode_wg_tasks",
-        "share_num", "share_den", "policy")]
+        "share_num", "share_den", "cu_prefill_slots", "policy")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -108,7 +108,7 @@ def status_string(status: int) -> str:
 def make_config(dtype=POD_BF16, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
                 sm_scale=0.0, max_chunk_len=4096, max_num_decode=256, max_context=32768,
                 max_total_context=0, wg_per_cu=0, prefill_split_cap_waves=0,
-                policy=POD_POLICY_PROPORTIONAL, device=-1) -> PodAttnConfig:
+                policy=POD_POLICY_CU_BALANCED, device=-1) -> PodAttnConfig:
     return PodAttnConfig(dtype, num_q_heads, num_kv_heads, head_dim, page_size, sm_scale,
                          max_chunk_len, max_num_decode, max_context, max_total_context,
                          wg_per_cu, prefill_split_cap_waves, policy, device)

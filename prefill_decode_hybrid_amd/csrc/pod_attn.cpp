@@ -41,7 +41,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   if (!(c->sm_scale >= 0.0f) || !std::isfinite(c->sm_scale)) return POD_ERR_INVALID_ARG;
   if (c->wg_per_cu != 0 && c->wg_per_cu != 2) return POD_ERR_UNSUPPORTED;
   if (c->prefill_split_cap_waves < 0) return POD_ERR_INVALID_ARG;
-  if (c->policy < pod::kPolicyProportional || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
+  if (c->policy < pod::kPolicyCuBalanced || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
   lim.max_chunk_len = c->max_chunk_len;
   lim.max_num_decode = c->max_num_decode;
   lim.max_context = c->max_context;
@@ -71,6 +71,7 @@ void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
   st->decode_wg_tasks = pl.has_d ? pl.d_wg_tasks : 0;
   st->share_num = pl.share_num;
   st->share_den = pl.share_den;
+  st->cu_prefill_slots = pl.cu_prefill_slots;
   st->policy = pl.policy;
 }
 
@@ -159,6 +160,7 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
   }
   p.share_num = pl.share_num;
   p.share_den = pl.share_den;
+  p.cu_prefill_slots = pl.cu_prefill_slots;
   p.policy = pl.policy;
   p.grid = pl.grid;
 

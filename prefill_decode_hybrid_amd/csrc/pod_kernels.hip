@@ -779,16 +779,21 @@ DEV void prefill_issue_block(const char* kpool, const char* vpool, int64_t tok_b
   using C = PfBf16<D>;
   const int lane = lane_id();
   const int pos = lane % C::CH;
+  const int lrow = lane / C::CH;
 #pragma unroll
   for (int i = 0; i < C::IPW; ++i) {
     const int ins = wave_id() * C::IPW + i;
-    const int row = ins * C::RPI + lane / C::CH;
-    const int key = min(kb0 + row, Lp - 1);  // rows past the request re-read a valid key; masked later
-    const int64_t base = ((int64_t)pids[(key >> 4) - pg0] * kPageSize + (key & 15)) * tok_bytes;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(kpool + base + ((pos ^ (row & 7)) << 4)),
-                                     (lds_void_t*)(stage + ins * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(vpool + base + ((pos ^ (2 * (row & 3))) << 4)),
-                                     (lds_void_t*)(stage + C::OPB + ins * 1024), 16, 0, 0);
+    const int row = ins * C::RPI + lrow;
+    // An instruction's rows share one page.  Rows past the request re-read
+    // the request's last key (never a NaN tail slot); they are masked later.
+    const int first = min(kb0 + ins * C::RPI, Lp - 1);
+    const int page = __builtin_amdgcn_readfirstlane(pids[(first >> 4) - pg0]);
+    const int slot = min(kb0 + row, Lp - 1) & 15;
+    const int64_t pbase = (int64_t)page * kPageSize * tok_bytes;
+    const uint32_t koff = (uint32_t)(slot * tok_bytes) + ((pos ^ (row & 7)) << 4);
+    const uint32_t voff = (uint32_t)(slot * tok_bytes) + ((pos ^ (2 * (row & 3))) << 4);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(kpool + pbase + koff), (lds_void_t*)(stage + ins * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(vpool + pbase + voff), (lds_void_t*)(stage + C::OPB + ins * 1024), 16, 0, 0);
   }
 }
 
@@ -869,45 +874,34 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
     const int ksw = rl & 7;
     const int gq = lane >> 4, ti = lane & 15;
     const int th = gq >> 1, tdh = gq & 1, tk = ti >> 2, tj = ti & 3;
-    // The loop runs a multiple of NS blocks with the same DMA and barrier
-    // sequence in every step (steps past nblk only re-load the last block), so
-    // the compiler sees one straight-line wait pattern per stage buffer.
-    for (int b0 = 0; b0 < nblk; b0 += C::NS) {
+    const float c2 = p.scale_log2;
+
+    // S^T (32 keys x 32 rows) of the block in stage `st`, unscaled
+    auto qk = [&](const char* st) __attribute__((always_inline)) {
+      f32x16_t s;
 #pragma unroll
-    for (int u = 0; u < C::NS; ++u) {
-      const int b = b0 + u;
-      // this wave's loads of block b are done once at most NS-2 newer blocks remain in flight
-      wait_vm_lgkm<C::LPB * (C::NS - 2)>();
-      __builtin_amdgcn_s_barrier();
-      prefill_issue_block<D>(kpool, vpool, tok_bytes, pids, pg0, p.Lp,
-                             t.k0 + min(b + C::NS - 1, nblk - 1) * C::BN, lb.st[(u + C::NS - 1) % C::NS]);
-      const int kb0 = t.k0 + b * C::BN;
-      if (b >= nblk || kb0 >= t.kw) continue;
-      const char* st = lb.st[u];
-      // ---- scores S^T (32 keys x 32 rows)
-      f32x16_t sc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sc[j] = 0.0f;
+      for (int j = 0; j < 16; ++j) s[j] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + krow_off + (((2 * ks + half) ^ ksw) << 4));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
       }
-      // ---- scale, causal mask, online softmax (base 2; the max is raised
-      //      only when a score exceeds it by more than 8)
-      const bool need_mask = (kb0 + C::BN - 1) > (p.P0 + t.row0);
-      float mx = kNegInf;
+      return s;
+    };
+    // online softmax of one block (base 2; the running max is raised only when
+    // a scaled score exceeds it by more than 8), then O^T += V^T P^T
+    auto softmax_pv = [&](f32x16_t sc, const char* st, int kb0) __attribute__((always_inline)) {
+      if ((kb0 + C::BN - 1) > (p.P0 + t.row0)) {  // diagonal block: causal mask
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float s = sc[j] * p.scale_log2;
-        if (need_mask) {
+        for (int j = 0; j < 16; ++j) {
           const int key = kb0 + 8 * (j >> 2) + 4 * half + (j & 3);
-          s = key <= lim ? s : kNegInf;
+          sc[j] = key <= lim ? sc[j] : kNegInf;
         }
-        sc[j] = s;
-        mx = fmaxf(mx, s);
       }
-      mx = fmaxf(mx, xor_lane(mx, 32));
+      float mx = sc[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[j]);
+      mx = fmaxf(mx, xor_lane(mx, 32)) * c2;  // scale > 0: the max commutes with it
       if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
         const float mnew = fmaxf(m, mx);
         const float alpha = fast_exp2(m - safe_max(mnew));
@@ -918,21 +912,21 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
           for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
         m = mnew;
       }
-      const float mu = safe_max(m);
+      const float nmu = -safe_max(m);
       bf16x8_t pf[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         uint32_t w4[4];
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
-          const float e0 = fast_exp2(sc[8 * ks + 2 * q2] - mu);
-          const float e1 = fast_exp2(sc[8 * ks + 2 * q2 + 1] - mu);
+          const float e0 = fast_exp2(fmaf(sc[8 * ks + 2 * q2], c2, nmu));
+          const float e1 = fast_exp2(fmaf(sc[8 * ks + 2 * q2 + 1], c2, nmu));
           l += e0 + e1;
           w4[q2] = pack_bf16(e0, e1);
         }
         pf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
       }
-      // ---- O^T += V^T P^T: keys 16ks + 4th + tk (first read) and +8 (second)
+      // keys 16ks + 4th + tk (first transposing read) and + 8 (second)
       const char* vt = st + C::OPB;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -949,9 +943,34 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
         }
       }
-    }
-    }
+    };
 
+    // block 0 must be in LDS before the first QK: blocks 1 and 2 may still fly
+    wait_vm_lgkm<C::LPB * (C::NS - 2)>();
+    __builtin_amdgcn_s_barrier();
+    f32x16_t s_cur = qk(lb.st[0]);
+    // Step b: QK of block b+1 is issued ahead of the softmax and PV of block
+    // b, so the matrix cores work while the vector unit does the softmax.
+    // Steps past nblk keep the same DMA/barrier sequence (re-loading the last
+    // block) so every stage buffer sees one straight-line wait pattern.
+    for (int b0 = 0; b0 < nblk; b0 += C::NS) {
+#pragma unroll
+      for (int u = 0; u < C::NS; ++u) {
+        const int b = b0 + u;
+        // block b+1 has landed once at most one newer block is in flight
+        wait_vm_lgkm<C::LPB * (C::NS - 3)>();
+        __builtin_amdgcn_s_barrier();
+        prefill_issue_block<D>(kpool, vpool, tok_bytes, pids, pg0, p.Lp,
+                               t.k0 + min(b + C::NS - 1, nblk - 1) * C::BN, lb.st[(u + C::NS - 1) % C::NS]);
+        if (b < nblk) {
+          const int kb0 = t.k0 + b * C::BN;
+          f32x16_t s_next = s_cur;
+          if (b + 1 < nblk && kb0 + C::BN < t.kw) s_next = qk(lb.st[(u + 1) % C::NS]);
+          if (kb0 < t.kw) softmax_pv(s_cur, lb.st[u], kb0);
+          s_cur = s_next;
+        }
+      }
+    }
     wait_vmem();  // no DMA may still target this workgroup's LDS when it is reused
   }
   __syncthreads();
@@ -1151,43 +1170,89 @@ __global__ __launch_bounds__(256, (decode_min_blocks<E, G>())) void pod_decode_k
   decode_wg<E, D, G, decode_pf<E>()>(p, blockIdx.x, lb);
 }
 
-// Fused hybrid kernel.  Each workgroup takes a ticket on its CU's counter;
-// the ticket's position in a period of share_den decides the role so that
-// share_num of every share_den workgroups arriving on a CU run prefill,
-// prefill first (paper §4.1 and §5.4.2).  The task is then claimed from that
-// role's queue, or from the other queue once the first is exhausted; since
-// the grid equals the task count, every claim succeeds and every task runs
-// exactly once, with no workgroup ever waiting for another.
+// Claim a prefill task, starting with this XCD's queue.  Queue x holds tasks
+// x, x+8, x+16, ...; tasks are ordered kv head fastest, so with 8 kv heads
+// each XCD streams one kv head's keys through its own L2.  Exhausted queues
+// are skipped; false once every prefill task is taken.
+DEV bool claim_prefill(const PodParams& p, uint32_t xcc, int& task) {
+  for (int k = 0; k < kXcdQueues; ++k) {
+    const uint32_t x = (xcc + k) % kXcdQueues;
+    const uint32_t n = (uint32_t)p.p_tasks > x ? ((uint32_t)p.p_tasks - x + kXcdQueues - 1) / kXcdQueues : 0u;
+    if (__hip_atomic_load(p.ctrl + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+    const uint32_t i = atomicAdd(p.ctrl + x, 1u);
+    if (i < n) {
+      task = (int)(x + kXcdQueues * i);
+      return true;
+    }
+  }
+  return false;
+}
+
+DEV bool claim_decode(const PodParams& p, int& task) {
+  const uint32_t i = atomicAdd(p.ctrl + kCtrlDecodeHead, 1u);
+  task = (int)i;
+  return i < (uint32_t)p.d_wg_tasks;
+}
+
+// Fused hybrid kernel.  A regular grid of prefill tasks + decode workgroup
+// tasks is launched; each workgroup picks its role after dispatch from the
+// compute unit it landed on (paper §4.1) and then claims a task of that role,
+// or of the other role once the first is exhausted.  Since the grid equals
+// the task count every claim succeeds, every task runs exactly once, and no
+// workgroup ever waits for another.
+//   CU-balanced (default): the CU's word counts running prefill (low half)
+//     and decode (high half) workgroups; a workgroup takes prefill while
+//     fewer than cu_prefill_slots prefill workgroups run there, decode
+//     otherwise, and uncounts itself when done.
+//   proportional / half: the CU's ticket counter; ticket t mod share_den
+//     runs prefill for share_num of every share_den arrivals, prefill first
+//     (paper §5.4.2).
+//   static: workgroup id decides, without looking at the CU (paper §3.3).
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   POD_DECLARE_LDS(E, D);
   __shared__ int role_task[2];
+  __shared__ uint32_t cu_word;
   if (threadIdx.x == 0) {
-    int role, task;
+    int role, task = 0;
     if (p.policy == kPolicyStatic) {
       role = (int)blockIdx.x < p.p_tasks ? 0 : 1;
       task = role == 0 ? (int)blockIdx.x : (int)blockIdx.x - p.p_tasks;
     } else {
-      const uint32_t t = atomicAdd(p.tickets + cu_key(), 1u) % (uint32_t)p.share_den;
-      const uint32_t num = (uint32_t)p.share_num, den = (uint32_t)p.share_den;
-      const bool pre = ((t + 1) * num + den - 1) / den > (t * num + den - 1) / den;
-      role = pre ? 0 : 1;
-      uint32_t x = atomicAdd(p.ctrl + role, 1u);
-      const uint32_t lim = role == 0 ? (uint32_t)p.p_tasks : (uint32_t)p.d_wg_tasks;
-      if (x >= lim) {
-        role ^= 1;
-        x = atomicAdd(p.ctrl + role, 1u);
+      const uint32_t key = cu_key();
+      const uint32_t xcc = (key >> 8) & 7u;
+      uint32_t* word = p.tickets + key;
+      if (p.policy == kPolicyCuBalanced) {
+        uint32_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while (true) {
+          role = (old & 0xffffu) < (uint32_t)p.cu_prefill_slots ? 0 : 1;
+          const uint32_t nw = old + (role == 0 ? 1u : 0x10000u);
+          if (__hip_atomic_compare_exchange_strong(word, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT))
+            break;
+        }
+      } else {
+        const uint32_t t = atomicAdd(word, 1u) % (uint32_t)p.share_den;
+        const uint32_t num = (uint32_t)p.share_num, den = (uint32_t)p.share_den;
+        role = ((t + 1) * num + den - 1) / den > (t * num + den - 1) / den ? 0 : 1;
       }
-      task = (int)x;
+      const int want = role;
+      bool ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, task);
+      if (!ok) {
+        role ^= 1;
+        ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, task);
+      }
+      if (p.policy == kPolicyCuBalanced && role != want)  // recount under the role actually taken
+        atomicAdd(word, role == 0 ? 1u - 0x10000u : 0x10000u - 1u);
+      cu_word = key;
       // The claim has been performed (its value returned) before the claim
       // count is bumped, so the workgroup that sees every claim counted can
       // reset the queue heads for the next launch.
       wait_vmem();
-      const uint32_t done = atomicAdd(p.ctrl + 2, 1u);
+      const uint32_t done = atomicAdd(p.ctrl + kCtrlClaims, 1u);
       if (done == (uint32_t)p.grid - 1u) {
-        __hip_atomic_store(p.ctrl + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.ctrl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.ctrl + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 0; q <= kCtrlClaims; ++q)
+          __hip_atomic_store(p.ctrl + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     role_task[0] = role;
@@ -1199,6 +1264,10 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
     if (task < p.p_tasks) PfSel<E, D>::run(p, task, lb);
   } else {
     if (task < p.d_wg_tasks) decode_wg<E, D, G, fused_pf<E, G>()>(p, task, lb);
+  }
+  if (p.policy == kPolicyCuBalanced) {
+    __syncthreads();
+    if (threadIdx.x == 0) atomicSub(p.tickets + cu_word, role == 0 ? 1u : 0x10000u);
   }
 }
 

@@ -37,9 +37,9 @@ struct PodParams {
   uint32_t* d_cnt;   // [request][kv head] arrival counters, 0 between calls
 
   // fused launch
-  uint32_t* ctrl;     // [0] prefill queue head, [1] decode queue head, [2] claims done
-  uint32_t* tickets;  // per-CU ticket counters (never reset; the role rule is periodic)
-  int share_num, share_den, policy, grid;
+  uint32_t* ctrl;     // [0..7] per-XCD prefill queue heads, [8] decode head, [9] claims
+  uint32_t* tickets;  // per-CU words: ticket counters, or running prefill | decode << 16
+  int share_num, share_den, cu_prefill_slots, policy, grid;
 };
 
 enum { kKernelHybrid = 0, kKernelPrefill = 1, kKernelDecode = 2 };

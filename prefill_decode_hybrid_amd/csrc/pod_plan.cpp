@@ -161,6 +161,11 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     } else {
       reduce_share(pl.p_tasks, pl.d_wg_tasks, pl.share_num, pl.share_den);
     }
+    // prefill workgroups kept resident per CU: the proportional share of the
+    // CU's slots, at least one and leaving at least one for decode
+    const int64_t slots_cu = lim.wg_per_cu;
+    int64_t tp = std::llround((double)slots_cu * pl.share_num / pl.share_den);
+    pl.cu_prefill_slots = (int)std::max<int64_t>(1, std::min<int64_t>(slots_cu - 1, tp));
   } else {
     pl.share_num = pl.has_p ? 1 : 0;
     pl.share_den = 1;

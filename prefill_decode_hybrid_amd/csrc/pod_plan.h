@@ -19,7 +19,7 @@ namespace pod {
 
 enum { kBf16 = 0, kF32 = 1 };
 enum { kModeHybrid = 0, kModePrefill = 1, kModeDecode = 2 };
-enum { kPolicyProportional = 0, kPolicyHalf = 1, kPolicyStatic = 2 };
+enum { kPolicyCuBalanced = 0, kPolicyProportional = 1, kPolicyHalf = 2, kPolicyStatic = 3 };
 
 constexpr int kPageSize = 16;
 constexpr int kWavesPerWG = 4;
@@ -36,7 +36,7 @@ struct Shape {
 struct Limits {
   int max_chunk_len = 0, max_num_decode = 0, max_context = 0;
   int64_t max_total_context = 0;
-  int wg_per_cu = 2, cap_waves = 2, policy = kPolicyProportional;
+  int wg_per_cu = 2, cap_waves = 2, policy = kPolicyCuBalanced;
   int num_cus = 0;
   // capacities derived by workspace_layout()
   int64_t cap_prefill_tasks = 0, cap_wave_tasks = 0, cap_tiles = 0;
@@ -64,7 +64,7 @@ struct Plan {
   bool has_d = false;
   int N = 0, T = 0, d_wave_tasks = 0, d_wg_tasks = 0;
   // fused scheduling
-  int share_num = 0, share_den = 1, policy = 0;
+  int share_num = 0, share_den = 1, cu_prefill_slots = 0, policy = 0;
 };
 
 // Rows of one wave's query block and keys per staged KV block, per dtype.
@@ -88,5 +88,8 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p,
 
 constexpr int kTicketSlots = 2048;  // (xcc, se, sh, cu) keys
 constexpr int kCtrlWords = 64;
+constexpr int kXcdQueues = 8;      // per-XCD prefill queues: ctrl[0..7]
+constexpr int kCtrlDecodeHead = 8; // decode queue head
+constexpr int kCtrlClaims = 9;     // workgroups that have claimed a task
 
 }  // namespace pod

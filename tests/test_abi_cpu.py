@@ -176,34 +176,64 @@ def test_create_without_gpu_fails_cleanly(lib):
     assert rc == pod.POD_ERR_HIP and not h.value
 
 
-def simulate_fused_claims(n_p, n_d, num, den, n_cus, seed):
-    """Host model of the fused kernel's role pick and queue claims under a random
-    arrival order and random CU placement: returns the claimed (role, task) list."""
+def simulate_fused_claims(n_p, n_d, num, den, n_cus, seed, balanced=False, slots=1):
+    """Host model of the fused kernel's role pick and queue claims: per-CU
+    tickets or running counts, per-XCD prefill queues with stealing, one
+    decode queue, random arrival order and CU placement (running workgroups
+    finish at random).  Returns the claimed (role, task) list."""
     rng = random.Random(seed)
     tickets = [0] * n_cus
-    heads = [0, 0]
-    lim = [n_p, n_d]
+    running = [[] for _ in range(n_cus)]
+    heads = [0] * 8
+    dhead = 0
     claims = []
+
+    def claim_prefill(xcc):
+        for k in range(8):
+            x = (xcc + k) % 8
+            n = (n_p - x + 7) // 8 if n_p > x else 0
+            if heads[x] >= n:
+                continue
+            i = heads[x]
+            heads[x] += 1
+            if i < n:
+                return x + 8 * i
+        return None
+
     for _ in range(n_p + n_d):
         cu = rng.randrange(n_cus)
-        t = tickets[cu] % den
-        tickets[cu] += 1
-        role = 0 if ((t + 1) * num + den - 1) // den > (t * num + den - 1) // den else 1
-        x = heads[role]
-        heads[role] += 1
-        if x >= lim[role]:
+        if running[cu] and rng.random() < 0.5:
+            running[cu].pop(rng.randrange(len(running[cu])))
+        if balanced:
+            role = 0 if sum(1 for r in running[cu] if r == 0) < slots else 1
+        else:
+            t = tickets[cu] % den
+            tickets[cu] += 1
+            role = 0 if ((t + 1) * num + den - 1) // den > (t * num + den - 1) // den else 1
+        task = claim_prefill(cu % 8) if role == 0 else None
+        if role == 1:
+            task, dhead = dhead, dhead + 1
+            if task >= n_d:
+                task = None
+        if task is None:
             role ^= 1
-            x = heads[role]
-            heads[role] += 1
-        claims.append((role, x))
+            if role == 0:
+                task = claim_prefill(cu % 8)
+            else:
+                task, dhead = dhead, dhead + 1
+                task = task if task < n_d else None
+        assert task is not None, "a workgroup found no task"
+        running[cu].append(role)
+        claims.append((role, task))
     return claims
 
 
+@pytest.mark.parametrize("balanced", [False, True])
 @pytest.mark.parametrize("n_p,n_d,num,den", [(256, 2048, 7, 64), (1, 5, 1, 2), (40, 3, 63, 64),
-                                             (100, 100, 32, 64), (5, 1000, 1, 64)])
-def test_fused_claims_cover_every_task_once(n_p, n_d, num, den):
+                                             (100, 100, 32, 64), (5, 1000, 1, 64), (9, 9, 1, 2)])
+def test_fused_claims_cover_every_task_once(n_p, n_d, num, den, balanced):
     for seed in range(20):
-        claims = simulate_fused_claims(n_p, n_d, num, den, n_cus=8, seed=seed)
+        claims = simulate_fused_claims(n_p, n_d, num, den, n_cus=16, seed=seed, balanced=balanced)
         p = sorted(x for r, x in claims if r == 0)
         d = sorted(x for r, x in claims if r == 1)
         assert p == list(range(n_p)) and d == list(range(n_d))

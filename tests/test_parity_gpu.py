@@ -63,7 +63,7 @@ def test_small_cases(sp):
         run.close()
 
 
-@pytest.mark.parametrize("policy", [pod.POD_POLICY_HALF, pod.POD_POLICY_STATIC])
+@pytest.mark.parametrize("policy", [pod.POD_POLICY_PROPORTIONAL, pod.POD_POLICY_HALF, pod.POD_POLICY_STATIC])
 def test_policies_give_identical_results(policy):
     sp = SMALL[0]
     base = Run(inputs.make_batch(sp, seed=2))
