@@ -20,7 +20,6 @@ this path runs on one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -34,7 +33,6 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK = 2516.6e12   # dense bf16 MFMA, FLOP/s
 MFMA_F32_PEAK = 157.3e12
 HBM_PEAK = 8.0e12            # bytes/s
-KERNEL_SRC = os.path.join(ROOT, "prefill_decode_hybrid_amd", "csrc", "pod_kernels.hip")
 
 
 def log(*a):
@@ -55,14 +53,6 @@ def work_counts(b):
                 bytes_total=bytes_kv + bytes_qo)
 
 
-def kernel_hash():
-    h = hashlib.sha256()
-    for fn in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
-        if fn.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(os.path.dirname(KERNEL_SRC), fn), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None if
     they are missing or were taken on different kernel sources."""
@@ -70,7 +60,8 @@ def load_traffic(workload):
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("kernel_sources") != kernel_hash():
+    from prefill_decode_hybrid_amd.profiling import kernel_sources_hash
+    if t.get("kernel_sources") != kernel_sources_hash():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -89,38 +80,74 @@ def time_mode(fn, steps, flush, torch):
 
 
 def cpu_baseline(batch, seconds_target=12.0):
-    """The fp64 oracle on a bounded sample of the same batch, scaled to one batch."""
+    """The fp64 oracle on a bounded sample of the same batch, scaled to one batch.
+
+    A small probe sample sets the pace; the measured sample is then sized to
+    take about `seconds_target` seconds (capped at the whole batch), split
+    between prefill rows and decode requests in proportion to their work."""
     import numpy as np
     import oracle
     w = work_counts(batch)
     lens = batch.context_lens.numpy()
-    rng = np.random.default_rng(0)
-    n_req = min(len(lens), 4)
-    reqs = sorted(rng.choice(len(lens), size=n_req, replace=False).tolist())
-    n_rows = min(batch.chunk_len, 32)
-    rows = sorted(rng.choice(batch.chunk_len, size=n_rows, replace=False).tolist())
     hq, d = batch.num_q_heads, batch.head_dim
     C, P0 = batch.chunk_len, batch.chunk_offset
-    f_rows = 4.0 * d * hq * sum(P0 + r + 1 for r in rows)
-    f_reqs = 4.0 * d * hq * sum(int(lens[r]) for r in reqs)
+    rng = np.random.default_rng(0)
+    row_order = rng.permutation(C)
+    req_order = rng.permutation(len(lens))
     oracle.load()
-    t0 = time.perf_counter()
-    oracle.prefill(batch.q_prefill, batch.k_pool, batch.v_pool, batch.page_table_prefill, P0,
-                   batch.sm_scale, rows=rows)
-    t1 = time.perf_counter()
-    oracle.decode(batch.q_decode, batch.k_pool, batch.v_pool, batch.page_table_decode,
-                  batch.context_lens, batch.sm_scale, reqs=reqs)
-    t2 = time.perf_counter()
+
+    def run(n_rows, n_req):
+        rows = sorted(row_order[:n_rows].tolist())
+        reqs = sorted(req_order[:n_req].tolist())
+        f_rows = 4.0 * d * hq * sum(P0 + r + 1 for r in rows)
+        f_reqs = 4.0 * d * hq * sum(int(lens[r]) for r in reqs)
+        t0 = time.perf_counter()
+        if rows:
+            oracle.prefill(batch.q_prefill, batch.k_pool, batch.v_pool, batch.page_table_prefill, P0,
+                           batch.sm_scale, rows=rows)
+        t1 = time.perf_counter()
+        if reqs:
+            oracle.decode(batch.q_decode, batch.k_pool, batch.v_pool, batch.page_table_decode,
+                          batch.context_lens, batch.sm_scale, reqs=reqs)
+        t2 = time.perf_counter()
+        return rows, reqs, f_rows, f_reqs, t1 - t0, t2 - t1
+
+    # probe: a few rows and one request
+    _, _, fr, fq, tr, tq = run(min(C, 8), 1)
+    rate_p = fr / max(tr, 1e-6)   # oracle FLOP/s on prefill rows
+    rate_d = fq / max(tq, 1e-6)
+    t_full = w["f_prefill"] / rate_p + w["f_decode"] / rate_d
+    frac = min(1.0, seconds_target / max(t_full, 1e-9))
+    n_rows = max(1, min(C, int(round(C * frac))))
+    n_req = max(1, min(len(lens), int(round(len(lens) * frac))))
+    rows, reqs, f_rows, f_reqs, t_p, t_d = run(n_rows, n_req)
     # scale each half by its work ratio (visible query-key products)
-    t_batch = (t1 - t0) * (w["f_prefill"] / f_rows) + (t2 - t1) * (w["f_decode"] / f_reqs)
+    t_batch = t_p * (w["f_prefill"] / f_rows) + t_d * (w["f_decode"] / f_reqs)
     try:
         cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     except Exception:
         cores = os.cpu_count() or 1
     return {"value": round(t_batch * 1e6, 1), "unit": "us", "cores": cores, "kind": "oracle",
-            "sample": f"{n_rows} prefill rows x {hq} heads and {n_req} decode requests x {hq} heads of the "
-                      f"same batch, fp64 C+OpenMP, {t2 - t0:.1f} s measured, scaled by visible query-key "
-                      f"products to the whole batch"}
+            "sample": f"{len(rows)} of {C} prefill rows and {len(reqs)} of {len(lens)} decode requests "
+                      f"(all {hq} heads) of the same batch, fp64 C+OpenMP on {cores} threads, "
+                      f"{t_p + t_d:.1f} s measured, scaled by visible query-key products to the whole batch"}
+
+
+def counters_driver(att, dev, op, od, ctx_host, torch, reps=2):
+    """Run each entry point and a 512 MiB device copy a few times, untimed:
+    the workload for rocprofv3 counter passes (the copy calibrates the
+    FETCH_SIZE / WRITE_SIZE counters against a known byte count)."""
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        att.hybrid(dev, op, od, ctx_host)
+        torch.cuda.synchronize()
+        att.prefill_only(dev, op)
+        torch.cuda.synchronize()
+        att.decode_only(dev, od, ctx_host)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 def main():
@@ -132,6 +159,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-hybrid", action="store_true", help="skip the split-launch baselines")
+    ap.add_argument("--counters-driver", action="store_true",
+                    help="run each entry point untimed (the workload for rocprofv3 --pmc passes) and exit")
+    ap.add_argument("--policy", type=int, default=0, help="fused role policy (enum pod_policy)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this hot path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -141,6 +171,7 @@ def main():
     import torch
     import prefill_decode_hybrid_amd as pod
     from prefill_decode_hybrid_amd import inputs
+    from prefill_decode_hybrid_amd.profiling import kernel_sources_hash
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -152,11 +183,16 @@ def main():
     log(f"[bench] generated in {time.time() - t0:.1f}s: {inputs.describe(batch)}")
     dev = batch.to("cuda:0")
     ctx_host = batch.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(batch))
+    att = pod.PodAttention(pod.config_for_batch(batch, policy=args.policy))
     op = torch.empty_like(dev.q_prefill)
     od = torch.empty_like(dev.q_decode)
     op2 = torch.empty_like(dev.q_prefill)
     od2 = torch.empty_like(dev.q_decode)
+    if args.counters_driver:
+        counters_driver(att, dev, op, od, ctx_host, torch)
+        log("[bench] counters driver done")
+        att.close()
+        return
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
 
@@ -275,7 +311,7 @@ def main():
         "finite": finite,
         "plan": plan,
         "gpu": torch.cuda.get_device_name(0),
-        "kernel_sources": kernel_hash(),
+        "kernel_sources": kernel_sources_hash(),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")

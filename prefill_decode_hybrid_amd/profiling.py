@@ -1,0 +1,131 @@
+"""Summaries of rocprofv3 output for the hybrid-batch attention kernels.
+
+Turns a kernel-trace CSV and two counter-collection CSVs (one pass with
+FETCH_SIZE, one with WRITE_SIZE, both in KiB per dispatch) into a short text
+summary and a JSON record of the HBM bytes each kernel moves per launch.
+
+The counters are calibrated against a plain device-to-device copy of known
+size that the counter workload (``bench.py --counters-driver``) runs beside
+the kernels: true bytes = counter * (copy bytes / counter value of the copy).
+
+    python -m prefill_decode_hybrid_amd.profiling --workload NAME \
+        --trace DIR --fetch DIR --write DIR --out profiles/
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CALIB_BYTES = 512 << 20          # the counter workload's device copy (read and written once)
+CALIB_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_sources_hash() -> str:
+    """Hash of the HIP/C++ sources: counter data is tied to the code it measured."""
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    n = name.replace("void ", "").split("(")[0]
+    return n.replace("pod::", "")
+
+
+def _rows(path_or_dir: str, suffix: str):
+    files = [path_or_dir] if path_or_dir.endswith(".csv") else glob.glob(
+        os.path.join(path_or_dir, "**", f"*{suffix}"), recursive=True)
+    for f in files:
+        yield from csv.DictReader(open(f))
+
+
+def kernel_durations(trace: str) -> dict:
+    """Per kernel: number of dispatches and mean / median / min duration in us."""
+    d = defaultdict(list)
+    for r in _rows(trace, "kernel_trace.csv"):
+        d[short_name(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: {"calls": len(v), "mean_us": statistics.mean(v), "median_us": statistics.median(v),
+                "min_us": min(v)} for k, v in d.items()}
+
+
+def counter_values(path: str, counter: str) -> dict:
+    """Per kernel: mean counter value per dispatch (copies: only the calibration size)."""
+    d = defaultdict(list)
+    for r in _rows(path, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        if name.startswith(CALIB_KERNEL):
+            if int(r["Grid_Size"]) < 65536:  # small helper copies, not the calibration copy
+                continue
+        d[short_name(name)].append(float(r["Counter_Value"]))
+    return {k: statistics.mean(v) for k, v in d.items()}
+
+
+def traffic(fetch_dir: str, write_dir: str) -> dict:
+    fetch = counter_values(fetch_dir, "FETCH_SIZE")
+    write = counter_values(write_dir, "WRITE_SIZE")
+    f_cal = CALIB_BYTES / fetch[CALIB_KERNEL]
+    w_cal = CALIB_BYTES / write[CALIB_KERNEL]
+    out = {"fetch_bytes_per_kib": f_cal, "write_bytes_per_kib": w_cal, "kernels": {}}
+    for k in fetch:
+        if k == CALIB_KERNEL or k not in write:
+            continue
+        out["kernels"][k] = {"fetch_kib": fetch[k], "write_kib": write[k],
+                             "hbm_read_bytes": fetch[k] * f_cal, "hbm_write_bytes": write[k] * w_cal,
+                             "hbm_bytes": fetch[k] * f_cal + write[k] * w_cal}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--out", default="profiles")
+    ap.add_argument("--command", default="", help="the command lines that produced the inputs")
+    a = ap.parse_args()
+    dur = kernel_durations(a.trace)
+    tr = traffic(a.fetch, a.write)
+    src = kernel_sources_hash()
+    hybrid = next((k for k in tr["kernels"] if k.startswith("pod_hybrid_kernel")), None)
+    rec = {"workload": a.workload, "kernel_sources": src, "kernel": hybrid,
+           "hbm_bytes_per_launch": tr["kernels"][hybrid]["hbm_bytes"] if hybrid else None,
+           "calibration": {"copy_bytes": CALIB_BYTES, "fetch_bytes_per_kib": tr["fetch_bytes_per_kib"],
+                           "write_bytes_per_kib": tr["write_bytes_per_kib"]},
+           "kernels": tr["kernels"]}
+    os.makedirs(a.out, exist_ok=True)
+    json.dump(rec, open(os.path.join(a.out, f"traffic_{a.workload}.json"), "w"), indent=1)
+    lines = [f"# rocprofv3 summary: {a.workload}", "", f"kernel sources: `{src}`", ""]
+    if a.command:
+        lines += ["Commands:", "", "```", a.command, "```", ""]
+    lines += ["| kernel | calls | mean us | median us | min us | HBM read MB | HBM write MB |",
+              "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(dur.items(), key=lambda kv: -kv[1]["mean_us"]):
+        if not k.startswith("pod_"):
+            continue
+        t = tr["kernels"].get(k, {})
+        rd = f"{t['hbm_read_bytes'] / 1e6:.1f}" if t else ""
+        wr = f"{t['hbm_write_bytes'] / 1e6:.1f}" if t else ""
+        lines.append(f"| `{k}` | {v['calls']} | {v['mean_us']:.1f} | {v['median_us']:.1f} | {v['min_us']:.1f} | {rd} | {wr} |")
+    lines += ["", f"Counter calibration: a {CALIB_BYTES >> 20} MiB device copy reads "
+              f"{CALIB_BYTES / tr['fetch_bytes_per_kib'] :.0f} KiB of FETCH_SIZE and writes "
+              f"{CALIB_BYTES / tr['write_bytes_per_kib']:.0f} KiB of WRITE_SIZE, so one FETCH_SIZE KiB is "
+              f"{tr['fetch_bytes_per_kib']:.0f} bytes and one WRITE_SIZE KiB {tr['write_bytes_per_kib']:.0f} bytes."]
+    open(os.path.join(a.out, f"{a.workload}.md"), "w").write("\n".join(lines) + "\n")
+    print(json.dumps({"workload": a.workload, "hbm_bytes_per_launch": rec["hbm_bytes_per_launch"]}))
+
+
+if __name__ == "__main__":
+    main()
