@@ -79,7 +79,7 @@ enum pod_dtype { POD_BF16 = 0, POD_F32 = 1 };
  * proportional and 50:50 ticket sequences (§5.4.2) and a fixed split by
  * workgroup id, i.e. CTA-parallel fusion without SM awareness (§3.3). */
 enum pod_policy {
-    POD_POLICY_CU_BALANCED = 0,  /* per-CU running counts; prefill slots = plan share   */
+    POD_POLICY_CU_BALANCED = 0,  /* per-CU running counts; prefill slots from the batch  */
     POD_POLICY_PROPORTIONAL = 1, /* per-CU tickets, prefill share = prefill / all tasks */
     POD_POLICY_HALF = 2,         /* per-CU tickets alternating prefill and decode       */
     POD_POLICY_STATIC = 3        /* workgroup id decides the role, no CU awareness      */
@@ -101,6 +101,9 @@ typedef struct {
                                  workgroups (paper §4.2.3 caps splits at two waves); 0 -> 2 */
     int32_t policy;           /* enum pod_policy                                       */
     int32_t device;           /* HIP device ordinal; -1 selects the current device     */
+    int32_t prefill_slots_x256; /* CU-balanced policy: prefill workgroups kept running per
+                                 CU, in 1/256 of a workgroup (1 .. 256 * wg_per_cu); 0
+                                 selects the planner's choice from the batch            */
 } pod_attn_config;
 
 typedef struct {
@@ -140,7 +143,8 @@ typedef struct {
     int32_t decode_wave_tasks;  /* (request, kv head, token split) units, one wave each */
     int32_t decode_wg_tasks;    /* decode workgroups (4 wave tasks each)               */
     int32_t share_num, share_den; /* prefill share of each CU's tickets               */
-    int32_t cu_prefill_slots;   /* CU-balanced policy: prefill workgroups kept per CU  */
+    int32_t cu_prefill_x256;    /* CU-balanced policy: prefill workgroups kept per CU,
+                                   averaged over CUs, in 1/256                        */
     int32_t policy;
 } pod_attn_stats;
 

@@ -42,6 +42,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   if (c->wg_per_cu != 0 && c->wg_per_cu != 2) return POD_ERR_UNSUPPORTED;
   if (c->prefill_split_cap_waves < 0) return POD_ERR_INVALID_ARG;
   if (c->policy < pod::kPolicyCuBalanced || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
+  if (c->prefill_slots_x256 < 0 || c->prefill_slots_x256 > 2 * 256) return POD_ERR_INVALID_ARG;
   lim.max_chunk_len = c->max_chunk_len;
   lim.max_num_decode = c->max_num_decode;
   lim.max_context = c->max_context;
@@ -49,6 +50,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   lim.wg_per_cu = 2;
   lim.cap_waves = c->prefill_split_cap_waves ? c->prefill_split_cap_waves : 2;
   lim.policy = c->policy;
+  lim.slots_x256 = c->prefill_slots_x256;
   scale = c->sm_scale > 0.0f ? c->sm_scale : 1.0f / std::sqrt((float)s.d);
   return POD_OK;
 }
@@ -71,7 +73,7 @@ void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
   st->decode_wg_tasks = pl.has_d ? pl.d_wg_tasks : 0;
   st->share_num = pl.share_num;
   st->share_den = pl.share_den;
-  st->cu_prefill_slots = pl.cu_prefill_slots;
+  st->cu_prefill_x256 = pl.cu_prefill_x256;
   st->policy = pl.policy;
 }
 
@@ -156,11 +158,12 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
     p.N = pl.N;
     p.T = pl.T;
     p.d_wave_tasks = pl.d_wave_tasks;
+    p.d_units = pl.d_wave_tasks / s.hkv;
     p.d_wg_tasks = pl.d_wg_tasks;
   }
   p.share_num = pl.share_num;
   p.share_den = pl.share_den;
-  p.cu_prefill_slots = pl.cu_prefill_slots;
+  p.cu_prefill_x256 = pl.cu_prefill_x256;
   p.policy = pl.policy;
   p.grid = pl.grid;
 

@@ -31,6 +31,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 struct Bf16 {
   static constexpr int bytes = 2;
@@ -142,30 +145,6 @@ DEV void store_out(void* base, int64_t idx, float v) {
   }
 }
 
-// Split partials cross compute units on different XCDs, whose L2s are not
-// coherent with each other.  They are written and read with device-scope
-// accesses (sc1: written through to, and read from, the device coherence
-// point), so publishing them needs no L2 writeback or invalidate: a wave
-// waits until its device-scope stores have completed (vmcnt 0) and only then
-// bumps the arrival counter, and the last arriver reads them back with
-// device-scope loads after its counter update has returned.
-DEV void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-DEV float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-DEV void st_dev4(float* p, float a, float b, float c, float d) {
-  st_dev(p, a);
-  st_dev(p + 1, b);
-  st_dev(p + 2, c);
-  st_dev(p + 3, d);
-}
-// Wait until every vector memory operation this wave issued has completed.
-DEV void wait_vmem() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 DEV float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -177,41 +156,143 @@ DEV float wave_sum(float x) {
   return x;
 }
 
-// Merge the S split partials of one output row-head and store the row.
-// Split s lives at part0 + s * sstride: acc[0..D) unnormalised, m (base 2) at
-// +moff, l at +loff.  Weights w_s = 2^(m_s - max m) are formed one split per
-// lane; the weighted sum runs over the splits in index order (64 lanes cover
-// d), so the result does not depend on which split arrived last.
-template <class E, int D>
-DEV void merge_partials(const float* part0, int64_t sstride, int moff, int loff, int S, void* out,
-                        int64_t out_off) {
-  constexpr int EPL = D / 64;
+// Split partials cross compute units on different XCDs, whose L2s are not
+// coherent with each other.  They are written and read with device-scope
+// accesses (cache policy sc1: written through to, and read from, the device
+// coherence point), so publishing them needs no L2 writeback or invalidate:
+// a wave waits until its device-scope stores have completed (vmcnt 0) and
+// only then bumps the arrival counter, and the last arriver reads them back
+// with device-scope loads after its counter update has returned.  The
+// accesses go through buffer resources so that they can be 16 bytes wide.
+constexpr int kDevScope = 16;        // buffer cache-policy bit sc1 (device scope)
+constexpr int kMergeLdsBytes = 2048; // wave-private LDS a merge needs for its weights
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Buffer resource over `bytes` bytes from a wave-uniform base address.
+DEV Rsrc dev_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+DEV void st_dev4(Rsrc r, uint32_t off, float a, float b, float c, float d) {
+  const u32x4_t v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kDevScope);
+}
+DEV void st_dev1(Rsrc r, uint32_t off, float a) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, (int)off, 0, kDevScope);
+}
+DEV f32x4_t ld_dev4(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kDevScope));
+}
+// Device-scope load from a per-lane address (global_load sc1).
+DEV float ld_dev(const char* p) {
+  return __hip_atomic_load(reinterpret_cast<float*>(const_cast<char*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory operation this wave issued has completed.
+DEV void wait_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Order this wave's LDS writes before its later LDS reads by other lanes.
+DEV void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Merge the S split partials of R output rows and store the rows.  The
+// partial of split s is a block at part0 + s * sstride (bytes): acc [R][D]
+// fp32 at +acc_off (rows contiguous), m (base 2) [R] at +m_off, l [R] at
+// +l_off.  With M the largest m_s of a row, w_s = 2^(m_s - M), the row is
+// sum_s w_s acc_s / sum_s w_s l_s; the sums run over the splits in index
+// order, so the result does not depend on which split arrived last.  Output
+// row i (i < nrows) goes to out0 + i * out_stride elements.  Up to IF
+// 16-byte partial pieces per lane are loaded at once (more when a split's
+// block is smaller).  `wl` is wave-private LDS of kMergeLdsBytes.
+template <class E, int R, int D, int IF>
+DEV void merge_rows(const char* part0, int64_t sstride, uint32_t acc_off, uint32_t m_off, uint32_t l_off,
+                    int S, int nrows, char* out0, int64_t out_stride, float* wl) {
+  static_assert(R <= 64 && 64 % R == 0, "rows per merge");
+  constexpr int ITEMS = R * D / 4;                  // 16-byte pieces of one split's acc block
+  constexpr int NL = (ITEMS + 63) / 64;             // pieces per lane
+  constexpr int SC = kMergeLdsBytes / 4 / R;        // splits per chunk of LDS weights
+  constexpr int SB = NL >= IF ? 1 : IF / NL;        // splits whose pieces are loaded together
+  const uint32_t blk = (uint32_t)(l_off + R * 4 > acc_off + ITEMS * 16 ? l_off + R * 4 : acc_off + ITEMS * 16);
   const int lane = lane_id();
+  const int rr = lane % R;
+  auto split_rsrc = [&](int s) __attribute__((always_inline)) { return dev_rsrc(part0 + (int64_t)s * sstride, blk); };
+
+  // (split, row) pairs q = s R + row, one per lane at a time: per-lane addresses
   float M = kNegInf;
-  for (int s0 = 0; s0 < S; s0 += 64)
-    if (s0 + lane < S) M = fmaxf(M, ld_dev(part0 + (int64_t)(s0 + lane) * sstride + moff));
-  const float Mu = safe_max(wave_max(M));
-  float acc[EPL] = {};
-  float L = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    float w = 0.0f;
-    if (s0 + lane < S) {
-      const float* ps = part0 + (int64_t)(s0 + lane) * sstride;
-      w = fast_exp2(ld_dev(ps + moff) - Mu);
-      L += w * ld_dev(ps + loff);
-    }
-    const int n = min(64, S - s0);
-#pragma unroll 4
-    for (int k = 0; k < n; ++k) {
-      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-      const float* ps = part0 + (int64_t)(s0 + k) * sstride + lane * EPL;
+  for (int q = lane; q < S * R; q += 64) M = fmaxf(M, ld_dev(part0 + (int64_t)(q / R) * sstride + m_off + 4 * rr));
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wk, ld_dev(ps + e), acc[e]);
+  for (int o = R; o < 64; o <<= 1) M = fmaxf(M, xor_lane(M, o));
+  M = safe_max(M);
+
+  float L = 0.0f;
+  f32x4_t acc[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) acc[j] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < S; c0 += SC) {
+    const int sc = min(SC, S - c0);
+    for (int q = lane; q < sc * R; q += 64) {
+      const char* ps = part0 + (int64_t)(c0 + q / R) * sstride;
+      const float w = fast_exp2(ld_dev(ps + m_off + 4 * rr) - M);
+      L += w * ld_dev(ps + l_off + 4 * rr);
+      wl[q] = w;
+    }
+    wave_lds_sync();
+    for (int s0 = 0; s0 < sc; s0 += SB) {
+      f32x4_t v[SB][NL];
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const bool live = s0 + b < sc;
+        const Rsrc rs = split_rsrc(c0 + s0 + (live ? b : 0));
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const int it = j * 64 + lane;
+          v[b][j] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+          if (live && (ITEMS % 64 == 0 || it < ITEMS)) v[b][j] = ld_dev4(rs, acc_off + 16 * it);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        if (s0 + b >= sc) break;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const int row = (j * 64 + lane) * 4 / D;
+          const float w = wl[(s0 + b) * R + (row < R ? row : 0)];
+          acc[j] += w * v[b][j];
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+#pragma unroll
+  for (int o = R; o < 64; o <<= 1) L += xor_lane(L, o);
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int it = j * 64 + lane;
+    const int row = it * 4 / D, d = it * 4 % D;
+    const float inv = 1.0f / __shfl(L, row < R ? row : 0, 64);
+    if ((ITEMS % 64 == 0 || it < ITEMS) && row < nrows) {
+      char* o = out0 + ((int64_t)row * out_stride + d) * E::bytes;
+      const f32x4_t x = acc[j] * inv;
+      if constexpr (E::bytes == 2) {
+        uint2 w;
+        w.x = pack_bf16(x[0], x[1]);
+        w.y = pack_bf16(x[2], x[3]);
+        *reinterpret_cast<uint2*>(o) = w;
+      } else {
+        *reinterpret_cast<float4*>(o) = make_float4(x[0], x[1], x[2], x[3]);
+      }
     }
   }
-  const float inv = 1.0f / wave_sum(L);
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) store_out<E>(out, out_off + lane * EPL + e, acc[e] * inv);
 }
 
 // Count this wave's arrival after its partial stores completed; true for the
@@ -268,24 +349,37 @@ DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S) {
   return false;
 }
 
+// Decode partial records: [G][D] acc, [G] m, [G] l, padded to 16 bytes.  The
+// record of (request r, kv head g, split s) is g * units + (first unit of r)
+// + s, so the splits of one (r, g) are adjacent.
+template <int D, int G>
+struct DecRec {
+  static constexpr int FLOATS = (G * (D + 2) + 3) & ~3;
+  static constexpr uint32_t BYTES = FLOATS * 4;
+  static constexpr uint32_t M_OFF = G * D * 4, L_OFF = G * D * 4 + G * 4;
+};
+
+template <int D, int G>
+DEV Rsrc decode_record(const PodParams& p, int unit, int g) {
+  return dev_rsrc(reinterpret_cast<const char*>(p.d_part) + ((int64_t)g * p.d_units + unit) * DecRec<D, G>::BYTES,
+                  DecRec<D, G>::BYTES);
+}
+
 // Count this split's arrival at (r, g); the last of the S splits merges all
 // partials of (r, g) in split order and restores the counter to zero.
 template <class E, int D, int G>
-DEV void decode_finish(const PodParams& p, int r, int s, int S, int unit, int g) {
-  const int hkv = p.hkv;
-  uint32_t* cnt = p.d_cnt + (int64_t)r * hkv + g;
+DEV void decode_finish(const PodParams& p, int r, int s, int S, int unit, int g, float* wl) {
+  using Rc = DecRec<D, G>;
+  uint32_t* cnt = p.d_cnt + (int64_t)r * p.hkv + g;
   if (!arrive_last(cnt, (uint32_t)S)) return;
-  // splits of (r, g) are wave tasks (unit - s + s') * hkv + g
-  const float* part0 = p.d_part + ((int64_t)(unit - s) * hkv + g) * G * (D + 2);
-  const int64_t sstride = (int64_t)hkv * G * (D + 2);
-  for (int h = 0; h < G; ++h)
-    merge_partials<E, D>(part0 + h * D, sstride, G * D - h * D + h, G * D + G - h * D + h, S, p.od,
-                         ((int64_t)r * p.hq + (int64_t)g * G + h) * D);
+  const char* part0 = reinterpret_cast<const char*>(p.d_part) + ((int64_t)g * p.d_units + unit - s) * Rc::BYTES;
+  char* out0 = reinterpret_cast<char*>(p.od) + ((int64_t)r * p.hq + (int64_t)g * G) * D * E::bytes;
+  merge_rows<E, G, D, (E::bytes == 2 ? 16 : 4)>(part0, Rc::BYTES, 0, Rc::M_OFF, Rc::L_OFF, S, G, out0, D, wl);
   if (lane_id() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class E, int D, int G, int PF>
-DEV void decode_wave(const PodParams& p, int wt) {
+DEV void decode_wave(const PodParams& p, int wt, float* wl) {
   using Fr = DecFrag<E, D>;
   constexpr int EPL = Fr::EPL, DW = Fr::DW;
   const int lane = lane_id();
@@ -432,20 +526,23 @@ DEV void decode_wave(const PodParams& p, int wt) {
     return;
   }
 
-  // partial of this split: [G][D] acc, [G] m, [G] l
-  float* part = p.d_part + (int64_t)wt * G * (D + 2);
+  // partial of this split
+  using Rc = DecRec<D, G>;
+  const Rsrc rs = decode_record<D, G>(p, unit, g);
+  static_assert(EPL % 4 == 0, "16-byte partial stores");
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if ((h & 3) == slot) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) st_dev(part + h * D + j * EPL + e, acc[h][e]);
+      for (int e = 0; e < EPL; e += 4)
+        st_dev4(rs, (h * D + j * EPL + e) * 4, acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
       if (j == 0) {
-        st_dev(part + G * D + h, m[h]);
-        st_dev(part + G * D + G + h, l[h]);
+        st_dev1(rs, Rc::M_OFF + h * 4, m[h]);
+        st_dev1(rs, Rc::L_OFF + h * 4, l[h]);
       }
     }
   }
-  decode_finish<E, D, G>(p, r, s, S, unit, g);
+  decode_finish<E, D, G>(p, r, s, S, unit, g, wl);
 }
 
 // bf16 decode on MFMA (v_mfma_f32_16x16x32_bf16), 16 query-head columns of
@@ -479,9 +576,6 @@ struct DecMfma {
   static constexpr float kLazy = 8.0f;
 };
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 DEV int ksw(int row) { return row & 7; }        // K chunk swizzle (ds_read_b128 over 8 rows)
@@ -663,30 +757,29 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
     }
     return;
   }
-  float* part = p.d_part + (int64_t)wt * G * (D + 2);
+  using Rc = DecRec<D, G>;
+  const Rsrc rs = decode_record<D, G>(p, unit, g);
   if (h < G) {
 #pragma unroll
-    for (int b = 0; b < DB; ++b) st_dev4(part + h * D + 16 * b + 4 * q4, acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    for (int b = 0; b < DB; ++b) st_dev4(rs, (h * D + 16 * b + 4 * q4) * 4, acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
     if (q4 == 0) {
-      st_dev(part + G * D + h, m);
-      st_dev(part + G * D + G + h, l);
+      st_dev1(rs, Rc::M_OFF + h * 4, m);
+      st_dev1(rs, Rc::L_OFF + h * 4, l);
     }
   }
-  decode_finish<Bf16, D, G>(p, r, s, S, unit, g);
+  decode_finish<Bf16, D, G>(p, r, s, S, unit, g, reinterpret_cast<float*>(lds));
 }
 
 template <class E, int D, int G, int PF>
 DEV void decode_wg(const PodParams& p, int wg_task, const LdsBufs& lb) {
   const int wt = wg_task * kWavesPerWG + wave_id();
   if (wt >= p.d_wave_tasks) return;
+  const int w = wave_id();
+  char* buf = w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3];
   if constexpr (E::bytes == 2)
-  {
-    const int w = wave_id();
-    char* buf = w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3];
     decode_wave_mfma<D, G>(p, wt, buf);
-  }
   else
-    decode_wave<E, D, G, PF>(p, wt);
+    decode_wave<E, D, G, PF>(p, wt, reinterpret_cast<float*>(buf));
 }
 
 // ---------------------------------------------------------- prefill (a2, a4)
@@ -797,27 +890,37 @@ DEV void prefill_issue_block(const char* kpool, const char* vpool, int64_t tok_b
   }
 }
 
+// Prefill partial of one task (tile, split): acc [RH][D] fp32, m [RH], l [RH]
+// for the tile's RH = 4 * RPW row-heads, wave w owning rows [w RPW, (w+1) RPW).
+template <int D, int RPW>
+struct PfRec {
+  static constexpr int RH = RPW * kWavesPerWG;
+  static constexpr uint32_t BYTES = RH * (D + 2) * 4;
+  static DEV uint32_t acc_off(int w) { return (uint32_t)(w * RPW * D * 4); }
+  static DEV uint32_t m_off(int w) { return (uint32_t)(RH * D * 4 + w * RPW * 4); }
+  static DEV uint32_t l_off(int w) { return (uint32_t)(RH * (D + 1) * 4 + w * RPW * 4); }
+};
+
+
 // Tile-level arrival and merge, shared by both prefill flavours: every
 // thread waits for its own partial stores, the workgroup synchronises, one
 // thread counts the arrival, and the last split's workgroup merges.
 template <class E, int D, int RPW>
-DEV void prefill_finish_split(const PodParams& p, const TaskGeom& t, int task, int* flag) {
+DEV void prefill_finish_split(const PodParams& p, const TaskGeom& t, int task, const LdsBufs& lb) {
   wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) *flag = atomicAdd(p.p_cnt + t.tile, 1u) == (uint32_t)p.splits - 1u;
+  if (threadIdx.x == 0) *lb.flag = atomicAdd(p.p_cnt + t.tile, 1u) == (uint32_t)p.splits - 1u;
   __syncthreads();
-  if (!*flag) return;
+  if (!*lb.flag) return;
   const int w = wave_id();
-  const int64_t rowheads = (int64_t)RPW * kWavesPerWG;
+  using Rc = PfRec<D, RPW>;
   // Tasks of one tile differ only in their split: task = split * tiles + (tile
   // position), so split s of this tile is task - (split - s) * tiles.
-  const int64_t sstride = (int64_t)p.tiles * rowheads * (D + 2);
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int row = t.row0 + rr;
-    if (row >= p.C) break;
-    const float* first = p.p_part + ((int64_t)(task - t.split * p.tiles) * rowheads + w * RPW + rr) * (D + 2);
-    merge_partials<E, D>(first, sstride, D, D + 1, p.splits, p.op, ((int64_t)row * p.hq + t.head) * D);
-  }
+  const char* part0 = reinterpret_cast<const char*>(p.p_part) + (int64_t)(task - t.split * p.tiles) * Rc::BYTES;
+  char* out0 = reinterpret_cast<char*>(p.op) + ((int64_t)t.row0 * p.hq + t.head) * D * E::bytes;
+  float* wl = reinterpret_cast<float*>(w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3]);
+  merge_rows<E, RPW, D, 16>(part0, (int64_t)p.tiles * Rc::BYTES, Rc::acc_off(w), Rc::m_off(w), Rc::l_off(w), p.splits,
+                        min(RPW, p.C - t.row0), out0, (int64_t)p.hq * D, wl);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(p.p_cnt + t.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -993,18 +1096,21 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
     return;
   }
   // split partial: unnormalised acc, m (base 2), l
-  const int64_t rowheads = (int64_t)C::RPW * kWavesPerWG;
-  float* pr = p.p_part + ((int64_t)task * rowheads + wave_id() * C::RPW + rl) * (D + 2);
+  using Rc = PfRec<D, C::RPW>;
+  const int w = wave_id();
+  const Rsrc rs = dev_rsrc(reinterpret_cast<const char*>(p.p_part) + (int64_t)task * Rc::BYTES, Rc::BYTES);
+  const uint32_t ro = Rc::acc_off(w) + rl * D * 4;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq)
-      st_dev4(pr + 32 * db + 8 * jq + 4 * half, o[db][4 * jq], o[db][4 * jq + 1], o[db][4 * jq + 2], o[db][4 * jq + 3]);
+      st_dev4(rs, ro + (32 * db + 8 * jq + 4 * half) * 4, o[db][4 * jq], o[db][4 * jq + 1], o[db][4 * jq + 2],
+              o[db][4 * jq + 3]);
   if (half == 0) {
-    st_dev(pr + D, m);
-    st_dev(pr + D + 1, ltot);
+    st_dev1(rs, Rc::m_off(w) + rl * 4, m);
+    st_dev1(rs, Rc::l_off(w) + rl * 4, ltot);
   }
-  prefill_finish_split<Bf16, D, C::RPW>(p, t, task, lb.flag);
+  prefill_finish_split<Bf16, D, C::RPW>(p, t, task, lb);
 }
 
 // fp32 prefill tile (exact fp32, VALU): lane = one query row, K/V blocks of 32
@@ -1106,13 +1212,15 @@ DEV void prefill_tile_f32(const PodParams& p, int task, const LdsBufs& lb) {
     }
     return;
   }
-  const int64_t rowheads = (int64_t)C::RPW * kWavesPerWG;
-  float* pr = p.p_part + ((int64_t)task * rowheads + wave_id() * C::RPW + lane) * (D + 2);
+  using Rc = PfRec<D, C::RPW>;
+  const int w = wave_id();
+  const Rsrc rs = dev_rsrc(reinterpret_cast<const char*>(p.p_part) + (int64_t)task * Rc::BYTES, Rc::BYTES);
+  const uint32_t ro = Rc::acc_off(w) + lane * D * 4;
 #pragma unroll
-  for (int e = 0; e < D; e += 4) st_dev4(pr + e, acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-  st_dev(pr + D, m);
-  st_dev(pr + D + 1, l);
-  prefill_finish_split<F32, D, C::RPW>(p, t, task, lb.flag);
+  for (int e = 0; e < D; e += 4) st_dev4(rs, ro + e * 4, acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  st_dev1(rs, Rc::m_off(w) + lane * 4, m);
+  st_dev1(rs, Rc::l_off(w) + lane * 4, l);
+  prefill_finish_split<F32, D, C::RPW>(p, t, task, lb);
 }
 
 template <class E, int D>
@@ -1161,7 +1269,7 @@ __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(PodParams p) {
 
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, (decode_min_blocks<E, G>())) void pod_decode_kernel(PodParams p) {
-  constexpr int W = E::bytes == 2 ? DecMfma<D>::LDS_WAVE : 16;  // one V buffer per wave
+  constexpr int W = E::bytes == 2 ? DecMfma<D>::LDS_WAVE : kMergeLdsBytes;  // per wave
   __shared__ __attribute__((aligned(16))) char dbuf0[W];
   __shared__ __attribute__((aligned(16))) char dbuf1[W];
   __shared__ __attribute__((aligned(16))) char dbuf2[W];
@@ -1172,26 +1280,44 @@ __global__ __launch_bounds__(256, (decode_min_blocks<E, G>())) void pod_decode_k
 
 // Claim a prefill task, starting with this XCD's queue.  Queue x holds tasks
 // x, x+8, x+16, ...; tasks are ordered kv head fastest, so with 8 kv heads
-// each XCD streams one kv head's keys through its own L2.  Exhausted queues
-// are skipped; false once every prefill task is taken.
+// each XCD streams one kv head's keys through its own L2.  The own queue is
+// tried with one atomic (a head past the end is harmless: it is only
+// compared); then the other heads are read together and a non-empty queue
+// is tried.  False once every prefill task is taken; that is recorded so
+// later workgroups need not look again.
+DEV uint32_t ctrl_load(const PodParams& p, int q) {
+  return __hip_atomic_load(p.ctrl + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 DEV bool claim_prefill(const PodParams& p, uint32_t xcc, int& task) {
-  for (int k = 0; k < kXcdQueues; ++k) {
+  const uint32_t nt = (uint32_t)p.p_tasks;
+  auto qlen = [&](uint32_t x) { return nt > x ? (nt - x + kXcdQueues - 1) / kXcdQueues : 0u; };
+  uint32_t i = atomicAdd(p.ctrl + xcc, 1u);
+  if (i < qlen(xcc)) {
+    task = (int)(xcc + kXcdQueues * i);
+    return true;
+  }
+  uint32_t h[kXcdQueues];
+#pragma unroll
+  for (int x = 0; x < kXcdQueues; ++x) h[x] = ctrl_load(p, x);
+  for (int k = 1; k < kXcdQueues; ++k) {
     const uint32_t x = (xcc + k) % kXcdQueues;
-    const uint32_t n = (uint32_t)p.p_tasks > x ? ((uint32_t)p.p_tasks - x + kXcdQueues - 1) / kXcdQueues : 0u;
-    if (__hip_atomic_load(p.ctrl + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
-    const uint32_t i = atomicAdd(p.ctrl + x, 1u);
-    if (i < n) {
+    if (h[x] >= qlen(x)) continue;
+    i = atomicAdd(p.ctrl + x, 1u);
+    if (i < qlen(x)) {
       task = (int)(x + kXcdQueues * i);
       return true;
     }
   }
+  __hip_atomic_store(p.ctrl + kCtrlPrefillDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return false;
 }
 
 DEV bool claim_decode(const PodParams& p, int& task) {
   const uint32_t i = atomicAdd(p.ctrl + kCtrlDecodeHead, 1u);
   task = (int)i;
-  return i < (uint32_t)p.d_wg_tasks;
+  if (i < (uint32_t)p.d_wg_tasks) return true;
+  __hip_atomic_store(p.ctrl + kCtrlDecodeDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
 }
 
 // Fused hybrid kernel.  A regular grid of prefill tasks + decode workgroup
@@ -1202,8 +1328,10 @@ DEV bool claim_decode(const PodParams& p, int& task) {
 // workgroup ever waits for another.
 //   CU-balanced (default): the CU's word counts running prefill (low half)
 //     and decode (high half) workgroups; a workgroup takes prefill while
-//     fewer than cu_prefill_slots prefill workgroups run there, decode
-//     otherwise, and uncounts itself when done.
+//     fewer than the CU's prefill target run there, decode otherwise, and
+//     uncounts itself when done.  The targets are floor(x) or floor(x)+1
+//     per CU (by a hash of the CU id) so that they average x =
+//     cu_prefill_x256 / 256 over the chip.
 //   proportional / half: the CU's ticket counter; ticket t mod share_den
 //     runs prefill for share_num of every share_den arrivals, prefill first
 //     (paper §5.4.2).
@@ -1211,10 +1339,11 @@ DEV bool claim_decode(const PodParams& p, int& task) {
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   POD_DECLARE_LDS(E, D);
-  __shared__ int role_task[2];
+  __shared__ int role_task[3];
   __shared__ uint32_t cu_word;
   if (threadIdx.x == 0) {
     int role, task = 0;
+    bool counted = p.policy == kPolicyCuBalanced;
     if (p.policy == kPolicyStatic) {
       role = (int)blockIdx.x < p.p_tasks ? 0 : 1;
       task = role == 0 ? (int)blockIdx.x : (int)blockIdx.x - p.p_tasks;
@@ -1223,13 +1352,22 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
       const uint32_t xcc = (key >> 8) & 7u;
       uint32_t* word = p.tickets + key;
       if (p.policy == kPolicyCuBalanced) {
+        const uint32_t frac = ((key * 2654435761u) >> 24) & 255u;
+        const uint32_t target = ((uint32_t)p.cu_prefill_x256 >> 8) + (frac < ((uint32_t)p.cu_prefill_x256 & 255u) ? 1u : 0u);
         uint32_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        while (true) {
-          role = (old & 0xffffu) < (uint32_t)p.cu_prefill_slots ? 0 : 1;
-          const uint32_t nw = old + (role == 0 ? 1u : 0x10000u);
-          if (__hip_atomic_compare_exchange_strong(word, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT))
-            break;
+        const uint32_t pdone = ctrl_load(p, kCtrlPrefillDone), ddone = ctrl_load(p, kCtrlDecodeDone);
+        if (pdone | ddone) {
+          // one queue is empty: take the other, uncounted (the mix no longer matters)
+          role = pdone ? 1 : 0;
+          counted = false;
+        } else {
+          while (true) {
+            role = (old & 0xffffu) < target ? 0 : 1;
+            const uint32_t nw = old + (role == 0 ? 1u : 0x10000u);
+            if (__hip_atomic_compare_exchange_strong(word, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+              break;
+          }
         }
       } else {
         const uint32_t t = atomicAdd(word, 1u) % (uint32_t)p.share_den;
@@ -1242,7 +1380,7 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
         role ^= 1;
         ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, task);
       }
-      if (p.policy == kPolicyCuBalanced && role != want)  // recount under the role actually taken
+      if (counted && role != want)  // recount under the role actually taken
         atomicAdd(word, role == 0 ? 1u - 0x10000u : 0x10000u - 1u);
       cu_word = key;
       // The claim has been performed (its value returned) before the claim
@@ -1251,12 +1389,13 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
       wait_vmem();
       const uint32_t done = atomicAdd(p.ctrl + kCtrlClaims, 1u);
       if (done == (uint32_t)p.grid - 1u) {
-        for (int q = 0; q <= kCtrlClaims; ++q)
+        for (int q = 0; q <= kCtrlDecodeDone; ++q)
           __hip_atomic_store(p.ctrl + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     role_task[0] = role;
     role_task[1] = task;
+    role_task[2] = counted;
   }
   __syncthreads();
   const int role = role_task[0], task = role_task[1];
@@ -1265,7 +1404,7 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   } else {
     if (task < p.d_wg_tasks) decode_wg<E, D, G, fused_pf<E, G>()>(p, task, lb);
   }
-  if (p.policy == kPolicyCuBalanced) {
+  if (role_task[2]) {
     __syncthreads();
     if (threadIdx.x == 0) atomicSub(p.tickets + cu_word, role == 0 ? 1u : 0x10000u);
   }

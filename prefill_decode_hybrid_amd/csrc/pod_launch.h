@@ -24,7 +24,7 @@ struct PodParams {
   const int32_t* pt_p;
   int C, P0, Lp;
   int rows_per_tile, heads_per_tile, row_blocks, head_groups, tiles, splits, split_keys, p_tasks;
-  float* p_part;     // [task][row-head in tile][d + 2] (acc..., m, l)
+  float* p_part;     // [task]: acc [row-head][d], m [row-head], l [row-head]
   uint32_t* p_cnt;   // [tile] arrival counters, 0 between calls
 
   // decode batch
@@ -32,14 +32,14 @@ struct PodParams {
   void* od;
   const int32_t* pt_d;
   const int32_t* ctx;
-  int stride, N, T, d_wave_tasks, d_wg_tasks;
-  float* d_part;     // [wave task][G][d], then [G] m, [G] l
+  int stride, N, T, d_units, d_wave_tasks, d_wg_tasks;
+  float* d_part;     // records [kv head][unit]: [G][d] acc, [G] m, [G] l, 16-byte padded
   uint32_t* d_cnt;   // [request][kv head] arrival counters, 0 between calls
 
   // fused launch
   uint32_t* ctrl;     // [0..7] per-XCD prefill queue heads, [8] decode head, [9] claims
   uint32_t* tickets;  // per-CU words: ticket counters, or running prefill | decode << 16
-  int share_num, share_den, cu_prefill_slots, policy, grid;
+  int share_num, share_den, cu_prefill_x256, policy, grid;
 };
 
 enum { kKernelHybrid = 0, kKernelPrefill = 1, kKernelDecode = 2 };

@@ -64,7 +64,8 @@ WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim) {
   at = align(at + (size_t)lim.cap_prefill_tasks * rowheads * (s.d + 2) * 4);
   w.d_part = at;
   const int G = s.hq / s.hkv;
-  at = align(at + (size_t)std::max<int64_t>(1, lim.cap_wave_tasks) * G * (s.d + 2) * 4);
+  const size_t rec = ((size_t)G * (s.d + 2) + 3) & ~size_t(3);  // 16-byte records
+  at = align(at + (size_t)std::max<int64_t>(1, lim.cap_wave_tasks) * rec * 4);
   w.total = at;
   return w;
 }
@@ -141,7 +142,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
                                                   : (int64_t)lim.max_num_decode * lim.max_context;
     if (total > cap_total) return POD_ERR_INVALID_ARG;
     pl.N = d.N;
-    const int64_t target = 4LL * lim.num_cus * 8;  // wave tasks: ~4 per resident wave slot
+    const int64_t target = 2LL * lim.num_cus * 8;  // wave tasks: ~2 per resident wave slot
     int64_t T = round_up(ceil_div(total * s.hkv, target), kPageSize);
     T = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(kMinSplitTokens, T));
     pl.T = (int)T;
@@ -161,11 +162,35 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     } else {
       reduce_share(pl.p_tasks, pl.d_wg_tasks, pl.share_num, pl.share_den);
     }
-    // prefill workgroups kept resident per CU: the proportional share of the
-    // CU's slots, at least one and leaving at least one for decode
-    const int64_t slots_cu = lim.wg_per_cu;
-    int64_t tp = std::llround((double)slots_cu * pl.share_num / pl.share_den);
-    pl.cu_prefill_slots = (int)std::max<int64_t>(1, std::min<int64_t>(slots_cu - 1, tp));
+    // Prefill workgroups kept running per CU (CU-balanced policy), in 1/256
+    // of a workgroup.  One decode workgroup per CU already streams KV at the
+    // chip's bandwidth, while a prefill tile runs about 1.45x slower with one
+    // workgroup per CU than with two.  So from the time each role needs alone
+    // (prefill: its FLOPs at the tile's rate, or one task's duration if the
+    // chunk has few tasks):
+    //  * prefill longer: prefill takes every slot and decode fills its tail;
+    //  * decode longer, prefill not negligible and the batch large: one slot
+    //    each, the roles overlap on every CU (the method's premise);
+    //  * prefill short next to decode: decode first, prefill fills the tail;
+    //  * otherwise (a small batch): as many prefill slots as prefill tasks,
+    //    so every tile starts at once beside the decodes.
+    const double es = s.dtype == kBf16 ? 2.0 : 4.0;
+    const double f_p = 4.0 * s.d * s.hq * ((double)pl.C * pl.P0 + 0.5 * pl.C * (pl.C + 1.0));
+    double lsum = 0.0;
+    for (int r = 0; r < d.N; ++r) lsum += d.ctx_host[r];
+    const double t_task = (double)std::min(pl.Lp, pl.split_keys) * kPrefillSecondsPerKey;
+    const double t_p = std::max(t_task, f_p / (s.dtype == kBf16 ? kPrefillFlopsBf16 : kPrefillFlopsF32));
+    const double t_d = 2.0 * s.hkv * s.d * es * lsum / kDecodeBytesPerS;
+    if (lim.slots_x256 > 0)
+      pl.cu_prefill_x256 = lim.slots_x256;
+    else if (t_p >= t_d)
+      pl.cu_prefill_x256 = 256 * lim.wg_per_cu;
+    else if (4.0 * t_p >= t_d && t_d >= kOverlapMinSeconds)
+      pl.cu_prefill_x256 = 256;
+    else if (10.0 * t_p <= t_d)
+      pl.cu_prefill_x256 = 0;
+    else
+      pl.cu_prefill_x256 = (int)std::max<int64_t>(1, std::min<int64_t>(256, 256LL * pl.p_tasks / lim.num_cus));
   } else {
     pl.share_num = pl.has_p ? 1 : 0;
     pl.share_den = 1;

@@ -26,8 +26,18 @@ constexpr int kWavesPerWG = 4;
 constexpr int kMaxSplitTokens = 1024;   // one lane per page id in a 64-lane wave
 constexpr int kMinSplitTokens = 256;
 constexpr int kMinPrefillSplitKeys = 1024;
-constexpr int kMaxSplitKeys = 32768;       // page ids of one split are staged in LDS
+constexpr int kMaxSplitKeys = 16384;       // page ids of one split are staged in LDS
 constexpr int kShareDen = 64;
+// Throughput of the split kernels on MI355X, used only to pick the fused
+// launch's per-CU prefill slots: prefill FLOP/s (bf16 and fp32 tiles) and
+// decode bytes/s over the whole chip, and the decode time below which a
+// batch is too small to gain from running the roles side by side.  The
+// choice changes where tasks run, never the result.
+constexpr double kPrefillFlopsBf16 = 7.5e14;
+constexpr double kPrefillFlopsF32 = 1.0e13;
+constexpr double kDecodeBytesPerS = 5.8e12;
+constexpr double kOverlapMinSeconds = 200e-6;
+constexpr double kPrefillSecondsPerKey = 39e-9;  // one bf16 tile task, two workgroups per CU
 
 struct Shape {
   int dtype = kBf16, hq = 0, hkv = 0, G = 0, d = 0, page = kPageSize;
@@ -37,6 +47,7 @@ struct Limits {
   int max_chunk_len = 0, max_num_decode = 0, max_context = 0;
   int64_t max_total_context = 0;
   int wg_per_cu = 2, cap_waves = 2, policy = kPolicyCuBalanced;
+  int slots_x256 = 0;  // prefill slots per CU for the CU-balanced policy; 0: from the batch
   int num_cus = 0;
   // capacities derived by workspace_layout()
   int64_t cap_prefill_tasks = 0, cap_wave_tasks = 0, cap_tiles = 0;
@@ -64,7 +75,7 @@ struct Plan {
   bool has_d = false;
   int N = 0, T = 0, d_wave_tasks = 0, d_wg_tasks = 0;
   // fused scheduling
-  int share_num = 0, share_den = 1, cu_prefill_slots = 0, policy = 0;
+  int share_num = 0, share_den = 1, cu_prefill_x256 = 0, policy = 0;
 };
 
 // Rows of one wave's query block and keys per staged KV block, per dtype.
@@ -91,5 +102,7 @@ constexpr int kCtrlWords = 64;
 constexpr int kXcdQueues = 8;      // per-XCD prefill queues: ctrl[0..7]
 constexpr int kCtrlDecodeHead = 8; // decode queue head
 constexpr int kCtrlClaims = 9;     // workgroups that have claimed a task
+constexpr int kCtrlPrefillDone = 10;  // set once a claim found every prefill queue empty
+constexpr int kCtrlDecodeDone = 11;   // set once a claim found the decode queue empty
 
 }  // namespace pod

@@ -90,7 +90,8 @@ def test_plan_invariants_on_configs(cid):
     assert (st["prefill_splits"] - 1) * st["prefill_split_keys"] < Lp
     assert st["prefill_tasks"] == st["prefill_tiles"] * st["prefill_splits"]
     slots = 256 * st["wg_per_cu"]
-    if st["prefill_splits"] > 1:  # the split cap: at most two waves of resident workgroups
+    assert st["prefill_split_keys"] <= 16384  # a split's page ids fit the LDS table
+    if st["prefill_splits"] > -(-Lp // 16384):  # splits for parallelism: at most two waves of workgroups
         assert st["prefill_tasks"] <= 2 * slots
     # decode: every (request, kv head) split into ceil(L / T) one-wave units
     T = st["decode_split_tokens"]
@@ -188,15 +189,21 @@ def simulate_fused_claims(n_p, n_d, num, den, n_cus, seed, balanced=False, slots
     dhead = 0
     claims = []
 
+    def qlen(x):
+        return (n_p - x + 7) // 8 if n_p > x else 0
+
     def claim_prefill(xcc):
-        for k in range(8):
+        i = heads[xcc]  # own queue: one atomic, a head past the end is harmless
+        heads[xcc] += 1
+        if i < qlen(xcc):
+            return xcc + 8 * i
+        for k in range(1, 8):
             x = (xcc + k) % 8
-            n = (n_p - x + 7) // 8 if n_p > x else 0
-            if heads[x] >= n:
+            if heads[x] >= qlen(x):
                 continue
             i = heads[x]
             heads[x] += 1
-            if i < n:
+            if i < qlen(x):
                 return x + 8 * i
         return None
 
