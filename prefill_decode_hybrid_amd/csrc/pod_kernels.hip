@@ -578,8 +578,22 @@ struct DecMfma {
 
 
 DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-DEV int ksw(int row) { return row & 7; }        // K chunk swizzle (ds_read_b128 over 8 rows)
-DEV int vsw(int row) { return 2 * (row & 3); }  // V chunk swizzle (transposing reads, 4 rows)
+// LDS chunk swizzles (measured on gfx950: 64 banks of 4 bytes, i.e. 256
+// bytes per bank row; a ds_read_b128 is served 16 lanes per pass, a
+// transposing ds_read_b64_tr_b16 32 lanes per pass).  Key rows of
+// RB = 16 / CH rows (CH 16-byte chunks per row) share a bank row.
+//  * K (both kernels): a b128 pass reads one logical chunk of 16 consecutive
+//    rows, so XOR the chunk with the row's bank-row index over all chunk bits.
+//  * V, prefill: a transposing pass reads 4 consecutive rows x 64 bytes, so
+//    the rows' 64-byte groups are spread: XOR 4 (row / RB).
+//  * V, decode: a transposing pass reads 8 consecutive rows x 32 bytes, so
+//    the rows' 32-byte pairs are spread: XOR 2 (row / RB).
+template <int CH>
+DEV int ksw_rows(int row) { return (row / (16 / CH)) & (CH - 1); }
+template <int CH>
+DEV int vsw_prefill(int row) { return 4 * ((row / (16 / CH)) & (CH / 4 - 1)); }
+template <int CH>
+DEV int vsw_decode(int row) { return 2 * ((row / (16 / CH)) & (CH / 2 - 1)); }
 
 template <int D, int G>
 DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
@@ -657,8 +671,8 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
       for (int u = 0; u < NI; ++u) {
         const int row = 16 * pp + u * C::RPI + lrow;
         const bool ok = kbase + row < t1;
-        *reinterpret_cast<u32x4_t*>(kl + row * C::ROWB + ((lchk ^ ksw(row)) << 4)) = kd[pp][u];
-        *reinterpret_cast<u32x4_t*>(vl + row * C::ROWB + ((lchk ^ vsw(row)) << 4)) =
+        *reinterpret_cast<u32x4_t*>(kl + row * C::ROWB + ((lchk ^ ksw_rows<C::CHR>(row)) << 4)) = kd[pp][u];
+        *reinterpret_cast<u32x4_t*>(vl + row * C::ROWB + ((lchk ^ vsw_decode<C::CHR>(row)) << 4)) =
             ok ? vd[pp][u] : (u32x4_t){0u, 0u, 0u, 0u};
       }
     // S^T for both pages
@@ -669,7 +683,7 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
       const int row = 16 * pp + kk;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + row * C::ROWB + (((4 * c + q4) ^ ksw(row)) << 4));
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + row * C::ROWB + (((4 * c + q4) ^ ksw_rows<C::CHR>(row)) << 4));
         sc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], sc[pp], 0, 0, 0);
       }
     }
@@ -712,9 +726,9 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
       const int chunk = 2 * b + (tj >> 1);
       const int r0 = 4 * q4 + tk, r1 = 16 + r0;
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(
-          vl + r0 * C::ROWB + ((chunk ^ vsw(r0)) << 4) + ((tj & 1) << 3)));
+          vl + r0 * C::ROWB + ((chunk ^ vsw_decode<C::CHR>(r0)) << 4) + ((tj & 1) << 3)));
       const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(
-          vl + r1 * C::ROWB + ((chunk ^ vsw(r1)) << 4) + ((tj & 1) << 3)));
+          vl + r1 * C::ROWB + ((chunk ^ vsw_decode<C::CHR>(r1)) << 4) + ((tj & 1) << 3)));
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (short __attribute__((ext_vector_type(8)))){
           lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc[b], 0, 0, 0);
@@ -883,8 +897,8 @@ DEV void prefill_issue_block(const char* kpool, const char* vpool, int64_t tok_b
     const int page = __builtin_amdgcn_readfirstlane(pids[(first >> 4) - pg0]);
     const int slot = min(kb0 + row, Lp - 1) & 15;
     const int64_t pbase = (int64_t)page * kPageSize * tok_bytes;
-    const uint32_t koff = (uint32_t)(slot * tok_bytes) + ((pos ^ (row & 7)) << 4);
-    const uint32_t voff = (uint32_t)(slot * tok_bytes) + ((pos ^ (2 * (row & 3))) << 4);
+    const uint32_t koff = (uint32_t)(slot * tok_bytes) + ((pos ^ ksw_rows<C::CH>(row)) << 4);
+    const uint32_t voff = (uint32_t)(slot * tok_bytes) + ((pos ^ vsw_prefill<C::CH>(row)) << 4);
     __builtin_amdgcn_global_load_lds((gbl_void_t*)(kpool + pbase + koff), (lds_void_t*)(stage + ins * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((gbl_void_t*)(vpool + pbase + voff), (lds_void_t*)(stage + C::OPB + ins * 1024), 16, 0, 0);
   }
@@ -974,7 +988,7 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
       prefill_issue_block<D>(kpool, vpool, tok_bytes, pids, pg0, p.Lp, t.k0 + min(s, nblk - 1) * C::BN, lb.st[s]);
     // per-lane LDS byte offsets of the MFMA operands inside a stage
     const int krow_off = rl * C::ROWB;
-    const int ksw = rl & 7;
+    const int ksw = ksw_rows<C::CH>(rl);
     const int gq = lane >> 4, ti = lane & 15;
     const int th = gq >> 1, tdh = gq & 1, tk = ti >> 2, tj = ti & 3;
     const float c2 = p.scale_log2;
@@ -1038,9 +1052,9 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
         for (int ks = 0; ks < 2; ++ks) {
           const int r0 = 16 * ks + 4 * th + tk, r1 = r0 + 8;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vt + r0 * C::ROWB + ((c ^ (2 * (r0 & 3))) << 4) + ((tj & 1) << 3)));
+              (__attribute__((address_space(3))) i16x4_t*)(vt + r0 * C::ROWB + ((c ^ vsw_prefill<C::CH>(r0)) << 4) + ((tj & 1) << 3)));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vt + r1 * C::ROWB + ((c ^ (2 * (r1 & 3))) << 4) + ((tj & 1) << 3)));
+              (__attribute__((address_space(3))) i16x4_t*)(vt + r1 * C::ROWB + ((c ^ vsw_prefill<C::CH>(r1)) << 4) + ((tj & 1) << 3)));
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (short __attribute__((ext_vector_type(8)))){
               lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
