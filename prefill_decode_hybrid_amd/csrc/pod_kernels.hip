@@ -43,6 +43,7 @@ struct F32 {
 };
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // The LDS a workgroup works in: four separately declared stage buffers (so
 // the compiler can tell which one an LDS-DMA load writes and never has to
@@ -880,27 +881,65 @@ struct PfBf16 {
   static_assert(IPW >= 1, "block too small for the workgroup");
 };
 
+// Per-lane byte offsets (within a page) of a wave's K and V DMA loads: load
+// i of the wave fetches 16-byte chunk pos ^ swizzle(row) of token slot row &
+// 15 into LDS row `row` of the block.  Blocks start on page boundaries, so
+// the offsets are the same for every block that lies inside the request.
 template <int D>
-DEV void prefill_issue_block(const char* kpool, const char* vpool, int64_t tok_bytes, const int* pids, int pg0,
-                             int Lp, int kb0, char* stage) {
+struct PfDma {
+  static constexpr int IPW = PfBf16<D>::IPW;
+  uint32_t k[IPW], v[IPW];
+};
+
+template <int D>
+DEV PfDma<D> prefill_dma_offsets(int64_t tok_bytes) {
   using C = PfBf16<D>;
   const int lane = lane_id();
-  const int pos = lane % C::CH;
-  const int lrow = lane / C::CH;
+  const int pos = lane % C::CH, lrow = lane / C::CH;
+  PfDma<D> o;
+#pragma unroll
+  for (int i = 0; i < C::IPW; ++i) {
+    const int row = (wave_id() * C::IPW + i) * C::RPI + lrow;
+    o.k[i] = (uint32_t)((row & 15) * tok_bytes) + ((pos ^ ksw_rows<C::CH>(row)) << 4);
+    o.v[i] = (uint32_t)((row & 15) * tok_bytes) + ((pos ^ vsw_prefill<C::CH>(row)) << 4);
+  }
+  return o;
+}
+
+// Page of the keys this wave loads for the block at kb0: a wave's loads
+// cover consecutive rows inside one page.  Rows past the request re-read its
+// last key (never a NaN tail slot); they are masked later.
+template <int D>
+DEV int prefill_wave_page_index(int kb0, int Lp, int pg0) {
+  using C = PfBf16<D>;
+  static_assert(C::IPW * C::RPI <= kPageSize, "a wave's rows must stay in one page");
+  return (min(kb0 + wave_id() * C::IPW * C::RPI, Lp - 1) >> 4) - pg0;
+}
+
+// Issue the DMA loads of the block at kb0 (page id `page` for this wave).
+template <int D>
+DEV void prefill_issue_block(const char* kpool, const char* vpool, int64_t tok_bytes, int page, int Lp, int kb0,
+                             const PfDma<D>& off, char* stage) {
+  using C = PfBf16<D>;
+  const char* kp = kpool + (int64_t)page * kPageSize * tok_bytes;
+  const char* vp = vpool + (int64_t)page * kPageSize * tok_bytes;
+  const bool tail = kb0 + C::BN > Lp;  // the block reaches past the request's last key
+  const int lane = lane_id();
+  const int pos = lane % C::CH, lrow = lane / C::CH;
+  // The DMA instructions stay outside any branch: only the offsets differ
+  // for a tail block, so the compiler keeps its per-buffer wait tracking.
 #pragma unroll
   for (int i = 0; i < C::IPW; ++i) {
     const int ins = wave_id() * C::IPW + i;
-    const int row = ins * C::RPI + lrow;
-    // An instruction's rows share one page.  Rows past the request re-read
-    // the request's last key (never a NaN tail slot); they are masked later.
-    const int first = min(kb0 + ins * C::RPI, Lp - 1);
-    const int page = __builtin_amdgcn_readfirstlane(pids[(first >> 4) - pg0]);
-    const int slot = min(kb0 + row, Lp - 1) & 15;
-    const int64_t pbase = (int64_t)page * kPageSize * tok_bytes;
-    const uint32_t koff = (uint32_t)(slot * tok_bytes) + ((pos ^ ksw_rows<C::CH>(row)) << 4);
-    const uint32_t voff = (uint32_t)(slot * tok_bytes) + ((pos ^ vsw_prefill<C::CH>(row)) << 4);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(kpool + pbase + koff), (lds_void_t*)(stage + ins * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(vpool + pbase + voff), (lds_void_t*)(stage + C::OPB + ins * 1024), 16, 0, 0);
+    uint32_t ko = off.k[i], vo = off.v[i];
+    if (tail) {
+      const int row = ins * C::RPI + lrow;
+      const uint32_t slot = (uint32_t)(min(kb0 + row, Lp - 1) & 15) * (uint32_t)tok_bytes;
+      ko = slot + ((pos ^ ksw_rows<C::CH>(row)) << 4);
+      vo = slot + ((pos ^ vsw_prefill<C::CH>(row)) << 4);
+    }
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(kp + ko), (lds_void_t*)(stage + ins * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(vp + vo), (lds_void_t*)(stage + C::OPB + ins * 1024), 16, 0, 0);
   }
 }
 
@@ -982,10 +1021,16 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
   __syncthreads();
 
   if (nblk > 0) {
+    const PfDma<D> dma = prefill_dma_offsets<D>(tok_bytes);
+    auto kb_of = [&](int b) __attribute__((always_inline)) { return t.k0 + min(b, nblk - 1) * C::BN; };
     // prologue: blocks 0 .. NS-2 (past the last block, the last block again)
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
-      prefill_issue_block<D>(kpool, vpool, tok_bytes, pids, pg0, p.Lp, t.k0 + min(s, nblk - 1) * C::BN, lb.st[s]);
+      prefill_issue_block<D>(kpool, vpool, tok_bytes,
+                             __builtin_amdgcn_readfirstlane(pids[prefill_wave_page_index<D>(kb_of(s), p.Lp, pg0)]),
+                             p.Lp, kb_of(s), dma, lb.st[s]);
+    // page id of the next block to issue, read one step ahead of its use
+    int pid_next = pids[prefill_wave_page_index<D>(kb_of(C::NS - 1), p.Lp, pg0)];
     // per-lane LDS byte offsets of the MFMA operands inside a stage
     const int krow_off = rl * C::ROWB;
     const int ksw = ksw_rows<C::CH>(rl);
@@ -1038,8 +1083,9 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
         for (int q2 = 0; q2 < 4; ++q2) {
           const float e0 = fast_exp2(fmaf(sc[8 * ks + 2 * q2], c2, nmu));
           const float e1 = fast_exp2(fmaf(sc[8 * ks + 2 * q2 + 1], c2, nmu));
-          l += e0 + e1;
           w4[q2] = pack_bf16(e0, e1);
+          // l sums the bf16 weights the PV product uses, so they normalise exactly
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4[q2]), kOnes2, l, false);
         }
         pf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
       }
@@ -1065,7 +1111,8 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
     // block 0 must be in LDS before the first QK: blocks 1 and 2 may still fly
     wait_vm_lgkm<C::LPB * (C::NS - 2)>();
     __builtin_amdgcn_s_barrier();
-    f32x16_t s_cur = qk(lb.st[0]);
+    // Scores of even blocks live in s_even, of odd blocks in s_odd (NS is even).
+    f32x16_t s_even = qk(lb.st[0]), s_odd;
     // Step b: QK of block b+1 is issued ahead of the softmax and PV of block
     // b, so the matrix cores work while the vector unit does the softmax.
     // Steps past nblk keep the same DMA/barrier sequence (re-loading the last
@@ -1077,14 +1124,20 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
         // block b+1 has landed once at most one newer block is in flight
         wait_vm_lgkm<C::LPB * (C::NS - 3)>();
         __builtin_amdgcn_s_barrier();
-        prefill_issue_block<D>(kpool, vpool, tok_bytes, pids, pg0, p.Lp,
-                               t.k0 + min(b + C::NS - 1, nblk - 1) * C::BN, lb.st[(u + C::NS - 1) % C::NS]);
+        const int page = __builtin_amdgcn_readfirstlane(pid_next);
+        prefill_issue_block<D>(kpool, vpool, tok_bytes, page, p.Lp, kb_of(b + C::NS - 1), dma,
+                               lb.st[(u + C::NS - 1) % C::NS]);
+        pid_next = pids[prefill_wave_page_index<D>(kb_of(b + C::NS), p.Lp, pg0)];
         if (b < nblk) {
           const int kb0 = t.k0 + b * C::BN;
-          f32x16_t s_next = s_cur;
-          if (b + 1 < nblk && kb0 + C::BN < t.kw) s_next = qk(lb.st[(u + 1) % C::NS]);
-          if (kb0 < t.kw) softmax_pv(s_cur, lb.st[u], kb0);
-          s_cur = s_next;
+          const bool next = b + 1 < nblk && kb0 + C::BN < t.kw;
+          if (u % 2 == 0) {
+            if (next) s_odd = qk(lb.st[(u + 1) % C::NS]);
+            if (kb0 < t.kw) softmax_pv(s_even, lb.st[u], kb0);
+          } else {
+            if (next) s_even = qk(lb.st[(u + 1) % C::NS]);
+            if (kb0 < t.kw) softmax_pv(s_odd, lb.st[u], kb0);
+          }
         }
       }
     }
