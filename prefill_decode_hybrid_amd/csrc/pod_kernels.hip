@@ -1050,9 +1050,11 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
       }
       return s;
     };
-    // online softmax of one block (base 2; the running max is raised only when
-    // a scaled score exceeds it by more than 8), then O^T += V^T P^T
-    auto softmax_pv = [&](f32x16_t sc, const char* st, int kb0) __attribute__((always_inline)) {
+    // Online softmax of one block (base 2; the running max is raised only when
+    // a scaled score exceeds it by more than 8), in two parts.  The first
+    // holds the rare branches: the causal mask of a diagonal block and the
+    // rescale of o and l; it returns -max.
+    auto softmax_max = [&](f32x16_t& sc, int kb0) __attribute__((always_inline)) {
       if ((kb0 + C::BN - 1) > (p.P0 + t.row0)) {  // diagonal block: causal mask
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -1074,7 +1076,13 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
           for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
         m = mnew;
       }
-      const float nmu = -safe_max(m);
+      return -safe_max(m);
+    };
+    // The second part is straight-line code: the weights of this block (vector
+    // unit), the QK of the next block (matrix cores, independent of the
+    // weights) and O^T += V^T P^T, so the scheduler can interleave them.
+    auto weights_qk_pv = [&](const f32x16_t& sc, float nmu, const char* st, f32x16_t& sn, const char* st_next)
+        __attribute__((always_inline)) {
       bf16x8_t pf[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -1089,6 +1097,7 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
         }
         pf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
       }
+      sn = qk(st_next);
       // keys 16ks + 4th + tk (first transposing read) and + 8 (second)
       const char* vt = st + C::OPB;
 #pragma unroll
@@ -1128,15 +1137,17 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
         prefill_issue_block<D>(kpool, vpool, tok_bytes, page, p.Lp, kb_of(b + C::NS - 1), dma,
                                lb.st[(u + C::NS - 1) % C::NS]);
         pid_next = pids[prefill_wave_page_index<D>(kb_of(b + C::NS), p.Lp, pg0)];
+        // Blocks past the wave's causal end are fully masked (weights 0), and
+        // the QK past the last block reads a stage that holds the last block
+        // again and is never used, so the body needs no further branches.
         if (b < nblk) {
           const int kb0 = t.k0 + b * C::BN;
-          const bool next = b + 1 < nblk && kb0 + C::BN < t.kw;
           if (u % 2 == 0) {
-            if (next) s_odd = qk(lb.st[(u + 1) % C::NS]);
-            if (kb0 < t.kw) softmax_pv(s_even, lb.st[u], kb0);
+            const float nmu = softmax_max(s_even, kb0);
+            weights_qk_pv(s_even, nmu, lb.st[u], s_odd, lb.st[(u + 1) % C::NS]);
           } else {
-            if (next) s_even = qk(lb.st[(u + 1) % C::NS]);
-            if (kb0 < t.kw) softmax_pv(s_odd, lb.st[u], kb0);
+            const float nmu = softmax_max(s_odd, kb0);
+            weights_qk_pv(s_odd, nmu, lb.st[u], s_even, lb.st[(u + 1) % C::NS]);
           }
         }
       }
