@@ -169,8 +169,11 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     // (prefill: its FLOPs at the tile's rate, or one task's duration if the
     // chunk has few tasks):
     //  * prefill longer: prefill takes every slot and decode fills its tail;
-    //  * decode longer, prefill not negligible and the batch large: one slot
-    //    each, the roles overlap on every CU (the method's premise);
+    //  * decode longer, prefill not negligible and the batch large: the roles
+    //    overlap on every CU (the method's premise) with 1.5 prefill slots per
+    //    CU on average: a decode workgroup beside a prefill one already
+    //    streams at close to its full rate, while the prefill keeps its tail
+    //    short (measured best on the 16K long-context batch: 1.25-1.5);
     //  * prefill short next to decode: decode first, prefill fills the tail;
     //  * otherwise (a small batch): as many prefill slots as prefill tasks,
     //    so every tile starts at once beside the decodes.
@@ -186,7 +189,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     else if (t_p >= t_d)
       pl.cu_prefill_x256 = 256 * lim.wg_per_cu;
     else if (4.0 * t_p >= t_d && t_d >= kOverlapMinSeconds)
-      pl.cu_prefill_x256 = 256;
+      pl.cu_prefill_x256 = 384;
     else if (10.0 * t_p <= t_d)
       pl.cu_prefill_x256 = 0;
     else
