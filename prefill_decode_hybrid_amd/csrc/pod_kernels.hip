@@ -1356,46 +1356,46 @@ __global__ __launch_bounds__(256, (decode_min_blocks<E, G>())) void pod_decode_k
   decode_wg<E, D, G, decode_pf<E>()>(p, blockIdx.x, lb);
 }
 
-// Claim a prefill task, starting with this XCD's queue.  Queue x holds tasks
-// x, x+8, x+16, ...; tasks are ordered kv head fastest, so with 8 kv heads
-// each XCD streams one kv head's keys through its own L2.  The own queue is
-// tried with one atomic (a head past the end is harmless: it is only
-// compared); then the other heads are read together and a non-empty queue
-// is tried.  False once every prefill task is taken; that is recorded so
-// later workgroups need not look again.
-DEV uint32_t ctrl_load(const PodParams& p, int q) {
-  return __hip_atomic_load(p.ctrl + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Per-XCD task queues: queue x of `heads` holds tasks x, x+8, x+16, ... of
+// n.  A claim first bumps the claimer's own queue (one atomic; a head past
+// the end is harmless, it is only compared), so claims spread over eight
+// words instead of contending on one; once that queue is empty the other
+// heads are read together and a non-empty queue is tried.  Prefill tasks are
+// ordered kv head fastest, so with 8 kv heads each XCD streams one kv head's
+// keys through its own L2.  n if every queue is empty; `done` then records
+// it so later workgroups need not look again.
+DEV uint32_t ctrl_load(const uint32_t* w) {
+  return __hip_atomic_load(const_cast<uint32_t*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-DEV bool claim_prefill(const PodParams& p, uint32_t xcc, int& task) {
-  const uint32_t nt = (uint32_t)p.p_tasks;
-  auto qlen = [&](uint32_t x) { return nt > x ? (nt - x + kXcdQueues - 1) / kXcdQueues : 0u; };
-  uint32_t i = atomicAdd(p.ctrl + xcc, 1u);
-  if (i < qlen(xcc)) {
-    task = (int)(xcc + kXcdQueues * i);
-    return true;
-  }
+DEV uint32_t xcd_queue_len(uint32_t n, uint32_t x) {
+  return n > x ? (n - x + kXcdQueues - 1) / kXcdQueues : 0u;
+}
+DEV uint32_t claim_xcd(uint32_t* heads, uint32_t* done, uint32_t n, uint32_t xcc) {
+  uint32_t i = atomicAdd(heads + xcc, 1u);
+  if (i < xcd_queue_len(n, xcc)) return xcc + kXcdQueues * i;
   uint32_t h[kXcdQueues];
 #pragma unroll
-  for (int x = 0; x < kXcdQueues; ++x) h[x] = ctrl_load(p, x);
+  for (int x = 0; x < kXcdQueues; ++x) h[x] = ctrl_load(heads + x);
   for (int k = 1; k < kXcdQueues; ++k) {
     const uint32_t x = (xcc + k) % kXcdQueues;
-    if (h[x] >= qlen(x)) continue;
-    i = atomicAdd(p.ctrl + x, 1u);
-    if (i < qlen(x)) {
-      task = (int)(x + kXcdQueues * i);
-      return true;
-    }
+    if (h[x] >= xcd_queue_len(n, x)) continue;
+    i = atomicAdd(heads + x, 1u);
+    if (i < xcd_queue_len(n, x)) return x + kXcdQueues * i;
   }
-  __hip_atomic_store(p.ctrl + kCtrlPrefillDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return false;
+  __hip_atomic_store(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return n;
 }
 
-DEV bool claim_decode(const PodParams& p, int& task) {
-  const uint32_t i = atomicAdd(p.ctrl + kCtrlDecodeHead, 1u);
-  task = (int)i;
-  if (i < (uint32_t)p.d_wg_tasks) return true;
-  __hip_atomic_store(p.ctrl + kCtrlDecodeDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return false;
+DEV bool claim_prefill(const PodParams& p, uint32_t xcc, int& task) {
+  const uint32_t t = claim_xcd(p.ctrl + kCtrlPrefillHeads, p.ctrl + kCtrlPrefillDone, (uint32_t)p.p_tasks, xcc);
+  task = (int)t;
+  return t < (uint32_t)p.p_tasks;
+}
+
+DEV bool claim_decode(const PodParams& p, uint32_t xcc, int& task) {
+  const uint32_t t = claim_xcd(p.ctrl + kCtrlDecodeHeads, p.ctrl + kCtrlDecodeDone, (uint32_t)p.d_wg_tasks, xcc);
+  task = (int)t;
+  return t < (uint32_t)p.d_wg_tasks;
 }
 
 // Fused hybrid kernel.  A regular grid of prefill tasks + decode workgroup
@@ -1433,7 +1433,7 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
         const uint32_t frac = ((key * 2654435761u) >> 24) & 255u;
         const uint32_t target = ((uint32_t)p.cu_prefill_x256 >> 8) + (frac < ((uint32_t)p.cu_prefill_x256 & 255u) ? 1u : 0u);
         uint32_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t pdone = ctrl_load(p, kCtrlPrefillDone), ddone = ctrl_load(p, kCtrlDecodeDone);
+        const uint32_t pdone = ctrl_load(p.ctrl + kCtrlPrefillDone), ddone = ctrl_load(p.ctrl + kCtrlDecodeDone);
         if (pdone | ddone) {
           // one queue is empty: take the other, uncounted (the mix no longer matters)
           role = pdone ? 1 : 0;
@@ -1453,24 +1453,20 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
         role = ((t + 1) * num + den - 1) / den > (t * num + den - 1) / den ? 0 : 1;
       }
       const int want = role;
-      bool ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, task);
+      bool ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, xcc, task);
       if (!ok) {
         role ^= 1;
-        ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, task);
+        ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, xcc, task);
       }
       if (counted && role != want)  // recount under the role actually taken
         atomicAdd(word, role == 0 ? 1u - 0x10000u : 0x10000u - 1u);
       cu_word = key;
-      // The claim has been performed (its value returned) before the claim
-      // count is bumped, so the workgroup that sees every claim counted can
-      // reset the queue heads for the next launch.
-      wait_vmem();
-      const uint32_t done = atomicAdd(p.ctrl + kCtrlClaims, 1u);
-      if (done == (uint32_t)p.grid - 1u) {
-        for (int q = 0; q <= kCtrlDecodeDone; ++q)
-          __hip_atomic_store(p.ctrl + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
     }
+    // The previous launch on this handle used the other block and has
+    // finished (stream order); clear it for the next launch.
+    if (blockIdx.x == 0)
+      for (int q = 0; q < kCtrlUsed; ++q)
+        __hip_atomic_store(p.ctrl_next + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     role_task[0] = role;
     role_task[1] = task;
     role_task[2] = counted;

@@ -37,7 +37,8 @@ struct PodParams {
   uint32_t* d_cnt;   // [request][kv head] arrival counters, 0 between calls
 
   // fused launch
-  uint32_t* ctrl;     // [0..7] per-XCD prefill queue heads, [8] decode head, [9] claims
+  uint32_t* ctrl;     // this launch's control block (pod_plan.h kCtrl*)
+  uint32_t* ctrl_next;  // the other block, cleared by this launch for the next one
   uint32_t* tickets;  // per-CU words: ticket counters, or running prefill | decode << 16
   int share_num, share_den, cu_prefill_x256, policy, grid;
 };

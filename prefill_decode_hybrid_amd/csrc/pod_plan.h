@@ -99,10 +99,16 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p,
 
 constexpr int kTicketSlots = 2048;  // (xcc, se, sh, cu) keys
 constexpr int kCtrlWords = 64;
-constexpr int kXcdQueues = 8;      // per-XCD prefill queues: ctrl[0..7]
-constexpr int kCtrlDecodeHead = 8; // decode queue head
-constexpr int kCtrlClaims = 9;     // workgroups that have claimed a task
-constexpr int kCtrlPrefillDone = 10;  // set once a claim found every prefill queue empty
-constexpr int kCtrlDecodeDone = 11;   // set once a claim found the decode queue empty
+constexpr int kXcdQueues = 8;         // per-XCD task queues (queue x holds tasks x, x+8, ...)
+// Fused-launch control words.  Two blocks of kCtrlBlock words alternate
+// between consecutive launches on a handle: a launch runs on block
+// (launch count & 1) and clears the other block for the launch after it.
+constexpr int kCtrlBlock = 32;
+constexpr int kCtrlPrefillHeads = 0;  // [0..7] prefill queue heads
+constexpr int kCtrlDecodeHeads = 8;   // [8..15] decode workgroup-task queue heads
+constexpr int kCtrlPrefillDone = 16;  // set once a claim found every prefill queue empty
+constexpr int kCtrlDecodeDone = 17;   // set once a claim found every decode queue empty
+constexpr int kCtrlUsed = 18;         // words of a block that a launch may dirty
+static_assert(2 * kCtrlBlock <= kCtrlWords, "control blocks");
 
 }  // namespace pod

@@ -179,31 +179,33 @@ def test_create_without_gpu_fails_cleanly(lib):
 
 def simulate_fused_claims(n_p, n_d, num, den, n_cus, seed, balanced=False, slots=1):
     """Host model of the fused kernel's role pick and queue claims: per-CU
-    tickets or running counts, per-XCD prefill queues with stealing, one
-    decode queue, random arrival order and CU placement (running workgroups
-    finish at random).  Returns the claimed (role, task) list."""
+    tickets or running counts, per-XCD prefill and decode queues (own queue
+    with one atomic, then the others), random arrival order and CU placement
+    (running workgroups finish at random).  Returns the claimed (role, task)
+    list."""
     rng = random.Random(seed)
     tickets = [0] * n_cus
     running = [[] for _ in range(n_cus)]
-    heads = [0] * 8
-    dhead = 0
+    heads = {0: [0] * 8, 1: [0] * 8}
+    ntask = {0: n_p, 1: n_d}
     claims = []
 
-    def qlen(x):
-        return (n_p - x + 7) // 8 if n_p > x else 0
+    def qlen(n, x):
+        return (n - x + 7) // 8 if n > x else 0
 
-    def claim_prefill(xcc):
-        i = heads[xcc]  # own queue: one atomic, a head past the end is harmless
-        heads[xcc] += 1
-        if i < qlen(xcc):
+    def claim(role, xcc):
+        h, n = heads[role], ntask[role]
+        i = h[xcc]  # own queue: one atomic, a head past the end is harmless
+        h[xcc] += 1
+        if i < qlen(n, xcc):
             return xcc + 8 * i
         for k in range(1, 8):
             x = (xcc + k) % 8
-            if heads[x] >= qlen(x):
+            if h[x] >= qlen(n, x):
                 continue
-            i = heads[x]
-            heads[x] += 1
-            if i < qlen(x):
+            i = h[x]
+            h[x] += 1
+            if i < qlen(n, x):
                 return x + 8 * i
         return None
 
@@ -217,18 +219,10 @@ def simulate_fused_claims(n_p, n_d, num, den, n_cus, seed, balanced=False, slots
             t = tickets[cu] % den
             tickets[cu] += 1
             role = 0 if ((t + 1) * num + den - 1) // den > (t * num + den - 1) // den else 1
-        task = claim_prefill(cu % 8) if role == 0 else None
-        if role == 1:
-            task, dhead = dhead, dhead + 1
-            if task >= n_d:
-                task = None
+        task = claim(role, cu % 8)
         if task is None:
             role ^= 1
-            if role == 0:
-                task = claim_prefill(cu % 8)
-            else:
-                task, dhead = dhead, dhead + 1
-                task = task if task < n_d else None
+            task = claim(role, cu % 8)
         assert task is not None, "a workgroup found no task"
         running[cu].append(role)
         claims.append((role, task))
