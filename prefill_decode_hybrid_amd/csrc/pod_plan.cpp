@@ -169,12 +169,13 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     // (prefill: its FLOPs at the tile's rate, or one task's duration if the
     // chunk has few tasks):
     //  * prefill longer: prefill takes every slot and decode fills its tail;
-    //  * decode longer, prefill not negligible and the batch large: the roles
-    //    overlap on every CU (the method's premise) with 1.5 prefill slots per
-    //    CU on average: a decode workgroup beside a prefill one already
-    //    streams at close to its full rate, while the prefill keeps its tail
-    //    short (measured best on the 16K long-context batch: 1.25-1.5);
-    //  * prefill short next to decode: decode first, prefill fills the tail;
+    //  * prefill under 1/8 of decode: decode first, prefill fills the tail;
+    //  * otherwise, a large batch: the roles overlap on every CU (the
+    //    method's premise) with 1.5 prefill slots per CU on average -- a
+    //    decode workgroup beside a prefill one streams at close to its full
+    //    rate while the prefill keeps its tail short (measured best from the
+    //    long-context batch down to late 512-token chunks of a 16K prompt
+    //    beside 64 16K decodes);
     //  * otherwise (a small batch): as many prefill slots as prefill tasks,
     //    so every tile starts at once beside the decodes.
     const double es = s.dtype == kBf16 ? 2.0 : 4.0;
@@ -188,10 +189,10 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
       pl.cu_prefill_x256 = lim.slots_x256;
     else if (t_p >= t_d)
       pl.cu_prefill_x256 = 256 * lim.wg_per_cu;
-    else if (4.0 * t_p >= t_d && t_d >= kOverlapMinSeconds)
-      pl.cu_prefill_x256 = 384;
-    else if (10.0 * t_p <= t_d)
+    else if (8.0 * t_p < t_d)
       pl.cu_prefill_x256 = 0;
+    else if (t_d >= kOverlapMinSeconds)
+      pl.cu_prefill_x256 = 384;
     else
       pl.cu_prefill_x256 = (int)std::max<int64_t>(1, std::min<int64_t>(256, 256LL * pl.p_tasks / lim.num_cus));
   } else {
