@@ -94,7 +94,8 @@ typedef struct {
     float sm_scale;           /* softmax scale; 0 selects 1/sqrt(head_dim)             */
     int32_t max_chunk_len;    /* largest prefill chunk a call may pass                 */
     int32_t max_num_decode;   /* largest decode batch                                  */
-    int32_t max_context;      /* largest decode context and largest offset+chunk       */
+    int32_t max_context;      /* largest decode context and largest offset+chunk;
+                                 at most 261888 (POD_ERR_UNSUPPORTED above)            */
     int64_t max_total_context;/* largest sum of decode contexts; 0: max_num_decode*max_context */
     int32_t wg_per_cu;        /* co-resident workgroups per CU; 0 selects 2 (only 2 built) */
     int32_t prefill_split_cap_waves; /* cap on prefill tasks, in waves of resident

@@ -39,6 +39,8 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   if (rc) return rc;
   if (c->max_chunk_len < 1 || c->max_num_decode < 1 || c->max_context < 1 || c->max_total_context < 0)
     return POD_ERR_INVALID_ARG;
+  // a request has at most 1023 decode splits (the unit scan packs counts of 64 requests in 16 bits)
+  if ((int64_t)c->max_context > (int64_t)pod::kMaxContext) return POD_ERR_UNSUPPORTED;
   if (!(c->sm_scale >= 0.0f) || !std::isfinite(c->sm_scale)) return POD_ERR_INVALID_ARG;
   if (c->wg_per_cu != 0 && c->wg_per_cu != 2) return POD_ERR_UNSUPPORTED;
   if (c->prefill_split_cap_waves < 0) return POD_ERR_INVALID_ARG;
@@ -162,6 +164,7 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
     p.T = pl.T;
     p.d_wave_tasks = pl.d_wave_tasks;
     p.d_units = pl.d_wave_tasks / s.hkv;
+    p.d_full = pl.d_full;
     p.d_wg_tasks = pl.d_wg_tasks;
   }
   p.share_num = pl.share_num;

@@ -319,40 +319,52 @@ struct DecFrag {
   static constexpr int DW = EPL * E::bytes / 4;
 };
 
-// Find (request, split, splits) of decode unit `unit` by a wave-wide scan of
-// per-request split counts ceil(L / T) in request order.
-DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S) {
+// Decode units are numbered longest first: the full T-token splits of every
+// request (request by request), then each request's shorter remainder split
+// (L mod T tokens, if any), so the last tasks to be claimed are the short
+// ones.  Find (request r, split s, splits S of r, base = units of the
+// requests before r in request order) of `unit` by a wave-wide scan of the
+// per-request counts; `base + s` indexes the request's partial records.
+DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S, int& base) {
   const int lane = lane_id();
   const int maxlen = p.stride * kPageSize;
-  int base = 0;
+  const bool rem = unit >= p.d_full;
+  const int u = rem ? unit - p.d_full : unit;
+  int key_acc = 0, base_acc = 0;
   for (int c0 = 0; c0 < p.N; c0 += 64) {
     const int idx = c0 + lane;
     int L = idx < p.N ? min(p.ctx[idx], maxlen) : 0;
     L = max(L, 0);
-    const int cnt = (L + p.T - 1) / p.T;
-    int incl = cnt;
+    const int full = L / p.T, part = L % p.T ? 1 : 0;
+    // (units of the request) << 16 | (units of this phase); both < 2^16 per 64 requests
+    const int own = ((full + part) << 16) | (rem ? part : full);
+    int incl = own;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       int v = __shfl_up(incl, off, 64);
       if (lane >= off) incl += v;
     }
     const int total = __shfl(incl, 63, 64);
-    if (unit < base + total) {
-      const uint64_t hit = __ballot(base + incl > unit);
+    if (u < key_acc + (total & 0xffff)) {
+      const uint64_t hit = __ballot(key_acc + (incl & 0xffff) > u);
       const int first = __builtin_ctzll(hit);
+      const int f_incl = __shfl(incl, first, 64), f_own = __shfl(own, first, 64);
       r = c0 + first;
-      s = unit - base - (__shfl(incl, first, 64) - __shfl(cnt, first, 64));
-      S = __shfl(cnt, first, 64);
+      S = f_own >> 16;
+      s = rem ? S - 1 : u - key_acc - ((f_incl & 0xffff) - (f_own & 0xffff));
+      base = base_acc + (f_incl >> 16) - S;
       return true;
     }
-    base += total;
+    key_acc += total & 0xffff;
+    base_acc += total >> 16;
   }
   return false;
 }
 
 // Decode partial records: [G][D] acc, [G] m, [G] l, padded to 16 bytes.  The
-// record of (request r, kv head g, split s) is g * units + (first unit of r)
-// + s, so the splits of one (r, g) are adjacent.
+// record of (request r, kv head g, split s) is g * units + base(r) + s, with
+// base(r) the units of the requests before r, so the splits of one (r, g)
+// are adjacent.
 template <int D, int G>
 struct DecRec {
   static constexpr int FLOATS = (G * (D + 2) + 3) & ~3;
@@ -369,11 +381,11 @@ DEV Rsrc decode_record(const PodParams& p, int unit, int g) {
 // Count this split's arrival at (r, g); the last of the S splits merges all
 // partials of (r, g) in split order and restores the counter to zero.
 template <class E, int D, int G>
-DEV void decode_finish(const PodParams& p, int r, int s, int S, int unit, int g, float* wl) {
+DEV void decode_finish(const PodParams& p, int r, int S, int base, int g, float* wl) {
   using Rc = DecRec<D, G>;
   uint32_t* cnt = p.d_cnt + (int64_t)r * p.hkv + g;
   if (!arrive_last(cnt, (uint32_t)S)) return;
-  const char* part0 = reinterpret_cast<const char*>(p.d_part) + ((int64_t)g * p.d_units + unit - s) * Rc::BYTES;
+  const char* part0 = reinterpret_cast<const char*>(p.d_part) + ((int64_t)g * p.d_units + base) * Rc::BYTES;
   char* out0 = reinterpret_cast<char*>(p.od) + ((int64_t)r * p.hq + (int64_t)g * G) * D * E::bytes;
   merge_rows<E, G, D, (E::bytes == 2 ? 16 : 4)>(part0, Rc::BYTES, 0, Rc::M_OFF, Rc::L_OFF, S, G, out0, D, wl);
   if (lane_id() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -387,20 +399,36 @@ DEV void decode_wave(const PodParams& p, int wt, float* wl) {
   const int hkv = p.hkv;
   const int g = wt % hkv;
   const int unit = wt / hkv;
-  int r, s, S;
-  if (!locate_unit(p, unit, r, s, S)) return;
+  int r, s, S, base;
+  if (!locate_unit(p, unit, r, s, S, base)) return;
   r = __builtin_amdgcn_readfirstlane(r);
   s = __builtin_amdgcn_readfirstlane(s);
   S = __builtin_amdgcn_readfirstlane(S);
+  base = __builtin_amdgcn_readfirstlane(base);
   const int L = min(p.ctx[r], p.stride * kPageSize);
   const int t0 = s * p.T;
   const int t1 = min(t0 + p.T, L);
   const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
   const int slot = lane >> 4, j = lane & 15;
 
-  int pid = 0;
-  if (lane < npg) pid = p.pt_d[(int64_t)r * p.stride + t0 / kPageSize + lane];
-  pid = (int)min((uint32_t)pid, p.num_pages - 1u);
+  // page ids of the split: lane i holds pages i, 64 + i, 128 + i, ...
+  const int32_t* ptr = p.pt_d + (int64_t)r * p.stride + t0 / kPageSize;
+  int pid[kSplitIdRegs];
+#pragma unroll
+  for (int k = 0; k < kSplitIdRegs; ++k) {
+    int v = 0;
+    if (64 * k + lane < npg) v = ptr[64 * k + lane];
+    pid[k] = (int)min((uint32_t)v, p.num_pages - 1u);
+  }
+  auto page_id = [&](int i) __attribute__((always_inline)) {
+    const int l = i & 63, k = i >> 6;
+    int v = __builtin_amdgcn_readlane(pid[0], l);
+#pragma unroll
+    for (int j = 1; j < kSplitIdRegs; ++j)
+      if (k == j) v = __builtin_amdgcn_readlane(pid[j], l);
+    return v;
+  };
+
 
   uint32_t q[G][DW];
   {
@@ -428,7 +456,7 @@ DEV void decode_wave(const PodParams& p, int wt, float* wl) {
   uint32_t kr[NB][4][DW], vr[NB][4][DW];
 
   auto issue = [&](uint32_t (&kd)[4][DW], uint32_t (&vd)[4][DW], int i) __attribute__((always_inline)) {
-    const int64_t page = __builtin_amdgcn_readlane(pid, i);
+    const int64_t page = page_id(i);
     const int64_t off = page * page_bytes;
 #pragma unroll
     for (int u = 0; u < 4; ++u) load_dw<DW>(kd[u], kb + off + 4 * u * tok_bytes);
@@ -529,7 +557,7 @@ DEV void decode_wave(const PodParams& p, int wt, float* wl) {
 
   // partial of this split
   using Rc = DecRec<D, G>;
-  const Rsrc rs = decode_record<D, G>(p, unit, g);
+  const Rsrc rs = decode_record<D, G>(p, base + s, g);
   static_assert(EPL % 4 == 0, "16-byte partial stores");
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -543,7 +571,7 @@ DEV void decode_wave(const PodParams& p, int wt, float* wl) {
       }
     }
   }
-  decode_finish<E, D, G>(p, r, s, S, unit, g, wl);
+  decode_finish<E, D, G>(p, r, S, base, g, wl);
 }
 
 // bf16 decode on MFMA (v_mfma_f32_16x16x32_bf16), 16 query-head columns of
@@ -604,11 +632,12 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   const int hkv = p.hkv;
   const int g = wt % hkv;
   const int unit = wt / hkv;
-  int r, s, S;
-  if (!locate_unit(p, unit, r, s, S)) return;
+  int r, s, S, base;
+  if (!locate_unit(p, unit, r, s, S, base)) return;
   r = __builtin_amdgcn_readfirstlane(r);
   s = __builtin_amdgcn_readfirstlane(s);
   S = __builtin_amdgcn_readfirstlane(S);
+  base = __builtin_amdgcn_readfirstlane(base);
   const int L = min(p.ctx[r], p.stride * kPageSize);
   const int t0 = s * p.T;
   const int t1 = min(t0 + p.T, L);
@@ -617,9 +646,24 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   const int kk = lane & 15, q4 = lane >> 4;       // MFMA roles: key / head column, quad
   const int lrow = lane / C::CHR, lchk = lane % C::CHR;  // load role: row in group, chunk
 
-  int pid = 0;
-  if (lane < npg) pid = p.pt_d[(int64_t)r * p.stride + t0 / kPageSize + lane];
-  pid = (int)min((uint32_t)pid, p.num_pages - 1u);
+  // page ids of the split: lane i holds pages i, 64 + i, 128 + i, ...
+  const int32_t* ptr = p.pt_d + (int64_t)r * p.stride + t0 / kPageSize;
+  int pid[kSplitIdRegs];
+#pragma unroll
+  for (int k = 0; k < kSplitIdRegs; ++k) {
+    int v = 0;
+    if (64 * k + lane < npg) v = ptr[64 * k + lane];
+    pid[k] = (int)min((uint32_t)v, p.num_pages - 1u);
+  }
+  auto page_id = [&](int i) __attribute__((always_inline)) {
+    const int l = i & 63, k = i >> 6;
+    int v = __builtin_amdgcn_readlane(pid[0], l);
+#pragma unroll
+    for (int j = 1; j < kSplitIdRegs; ++j)
+      if (k == j) v = __builtin_amdgcn_readlane(pid[j], l);
+    return v;
+  };
+
 
   // Q^T operand: column = head kk (< G), rows d = 32c + 8q4 .. +8
   bf16x8_t qf[KC];
@@ -653,7 +697,7 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       const int pg = min(2 * pair + pp, npg - 1);
-      const int64_t off = (int64_t)__builtin_amdgcn_readlane(pid, pg) * page_bytes;
+      const int64_t off = (int64_t)page_id(pg) * page_bytes;
 #pragma unroll
       for (int u = 0; u < NI; ++u)
         kd[pp][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + off + u * C::RPI * tok_bytes));
@@ -773,7 +817,7 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
     return;
   }
   using Rc = DecRec<D, G>;
-  const Rsrc rs = decode_record<D, G>(p, unit, g);
+  const Rsrc rs = decode_record<D, G>(p, base + s, g);
   if (h < G) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) st_dev4(rs, (h * D + 16 * b + 4 * q4) * 4, acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
@@ -782,7 +826,7 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
       st_dev1(rs, Rc::L_OFF + h * 4, l);
     }
   }
-  decode_finish<Bf16, D, G>(p, r, s, S, unit, g, reinterpret_cast<float*>(lds));
+  decode_finish<Bf16, D, G>(p, r, S, base, g, reinterpret_cast<float*>(lds));
 }
 
 template <class E, int D, int G, int PF>

@@ -33,6 +33,7 @@ struct PodParams {
   const int32_t* pt_d;
   const int32_t* ctx;
   int stride, N, T, d_units, d_wave_tasks, d_wg_tasks;
+  int d_full;        // units that are full T-token splits (numbered before the remainders)
   float* d_part;     // records [kv head][unit]: [G][d] acc, [G] m, [G] l, 16-byte padded
   uint32_t* d_cnt;   // [request][kv head] arrival counters, 0 between calls
 

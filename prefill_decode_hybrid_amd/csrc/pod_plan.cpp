@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <vector>
 
 #include "../../include/pod_attn.h"
 
@@ -142,12 +143,66 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
                                                   : (int64_t)lim.max_num_decode * lim.max_context;
     if (total > cap_total) return POD_ERR_INVALID_ARG;
     pl.N = d.N;
-    const int64_t target = 2LL * lim.num_cus * 8;  // wave tasks: ~2 per resident wave slot
-    int64_t T = round_up(ceil_div(total * s.hkv, target), kPageSize);
+    pl.d_total = total;
+  }
+
+  // Prefill workgroups kept running per CU (CU-balanced policy), in 1/256
+  // of a workgroup.  One decode workgroup per CU already streams KV at the
+  // chip's bandwidth, while a prefill tile runs about 1.45x slower with one
+  // workgroup per CU than with two.  So from the time each role needs alone
+  // (prefill: its FLOPs at the tile's rate, or one task's duration if the
+  // chunk has few tasks):
+  //  * prefill longer: prefill takes every slot and decode fills its tail;
+  //  * prefill under 1/8 of decode: decode first, prefill fills the tail;
+  //  * otherwise, a large batch: the roles overlap on every CU (the
+  //    method's premise) with 1.5 prefill slots per CU on average -- a
+  //    decode workgroup beside a prefill one streams at close to its full
+  //    rate while the prefill keeps its tail short (measured best from the
+  //    long-context batch down to late 512-token chunks of a 16K prompt
+  //    beside 64 16K decodes);
+  //  * otherwise (a small batch): as many prefill slots as prefill tasks,
+  //    so every tile starts at once beside the decodes.
+  if (pl.has_p && pl.has_d) {
+    const double es = s.dtype == kBf16 ? 2.0 : 4.0;
+    const double f_p = 4.0 * s.d * s.hq * ((double)pl.C * pl.P0 + 0.5 * pl.C * (pl.C + 1.0));
+    const double t_task = (double)std::min(pl.Lp, pl.split_keys) * kPrefillSecondsPerKey;
+    const double t_p = std::max(t_task, f_p / (s.dtype == kBf16 ? kPrefillFlopsBf16 : kPrefillFlopsF32));
+    const double t_d = 2.0 * s.hkv * s.d * es * (double)pl.d_total / kDecodeBytesPerS;
+    if (lim.slots_x256 > 0)
+      pl.cu_prefill_x256 = lim.slots_x256;
+    else if (t_p >= t_d)
+      pl.cu_prefill_x256 = 256 * lim.wg_per_cu;
+    else if (8.0 * t_p < t_d)
+      pl.cu_prefill_x256 = 0;
+    else if (t_d >= kOverlapMinSeconds)
+      pl.cu_prefill_x256 = 384;
+    else
+      pl.cu_prefill_x256 = (int)std::max<int64_t>(1, std::min<int64_t>(256, 256LL * pl.p_tasks / lim.num_cus));
+  }
+
+  if (pl.has_d) {
+    // Decode token splits.  Every wave task pays a start (locate the unit,
+    // page ids, first loads) and a merge, so tasks are as long as the load
+    // balance allows: about one wave task per 1.6 resident decode waves, and
+    // no longer than the median context, so a batch of very unequal contexts
+    // keeps enough tasks to balance (measured: 4096-token splits beat 1024 by
+    // ~6% on the 64 x 16K batch; 2048 beat 1024 and 4096 on 256 log-uniform
+    // contexts; 512 beat 256 and 1024 on 32 contexts of 1-4K).  The split
+    // depends on the decode batch alone, so a decode's result is the same
+    // bits whether or not a prefill chunk shares its launch.
+    std::vector<int> lens(d.ctx_host, d.ctx_host + d.N);
+    std::nth_element(lens.begin(), lens.begin() + d.N / 2, lens.end());
+    const int64_t median = lens[d.N / 2];
+    const int64_t target = (int64_t)lim.num_cus * 5;
+    int64_t T = round_up(std::min(ceil_div(pl.d_total * s.hkv, target), median), kPageSize);
     T = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(kMinSplitTokens, T));
     pl.T = (int)T;
-    int64_t units = 0;
-    for (int r = 0; r < d.N; ++r) units += ceil_div(d.ctx_host[r], T);
+    int64_t units = 0, full = 0;
+    for (int r = 0; r < d.N; ++r) {
+      units += ceil_div(d.ctx_host[r], T);
+      full += d.ctx_host[r] / T;
+    }
+    pl.d_full = (int)full;
     int64_t wt = units * s.hkv;
     if (wt > lim.cap_wave_tasks || wt > (1LL << 30)) return POD_ERR_WORKSPACE;
     pl.d_wave_tasks = (int)wt;
@@ -162,39 +217,6 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     } else {
       reduce_share(pl.p_tasks, pl.d_wg_tasks, pl.share_num, pl.share_den);
     }
-    // Prefill workgroups kept running per CU (CU-balanced policy), in 1/256
-    // of a workgroup.  One decode workgroup per CU already streams KV at the
-    // chip's bandwidth, while a prefill tile runs about 1.45x slower with one
-    // workgroup per CU than with two.  So from the time each role needs alone
-    // (prefill: its FLOPs at the tile's rate, or one task's duration if the
-    // chunk has few tasks):
-    //  * prefill longer: prefill takes every slot and decode fills its tail;
-    //  * prefill under 1/8 of decode: decode first, prefill fills the tail;
-    //  * otherwise, a large batch: the roles overlap on every CU (the
-    //    method's premise) with 1.5 prefill slots per CU on average -- a
-    //    decode workgroup beside a prefill one streams at close to its full
-    //    rate while the prefill keeps its tail short (measured best from the
-    //    long-context batch down to late 512-token chunks of a 16K prompt
-    //    beside 64 16K decodes);
-    //  * otherwise (a small batch): as many prefill slots as prefill tasks,
-    //    so every tile starts at once beside the decodes.
-    const double es = s.dtype == kBf16 ? 2.0 : 4.0;
-    const double f_p = 4.0 * s.d * s.hq * ((double)pl.C * pl.P0 + 0.5 * pl.C * (pl.C + 1.0));
-    double lsum = 0.0;
-    for (int r = 0; r < d.N; ++r) lsum += d.ctx_host[r];
-    const double t_task = (double)std::min(pl.Lp, pl.split_keys) * kPrefillSecondsPerKey;
-    const double t_p = std::max(t_task, f_p / (s.dtype == kBf16 ? kPrefillFlopsBf16 : kPrefillFlopsF32));
-    const double t_d = 2.0 * s.hkv * s.d * es * lsum / kDecodeBytesPerS;
-    if (lim.slots_x256 > 0)
-      pl.cu_prefill_x256 = lim.slots_x256;
-    else if (t_p >= t_d)
-      pl.cu_prefill_x256 = 256 * lim.wg_per_cu;
-    else if (8.0 * t_p < t_d)
-      pl.cu_prefill_x256 = 0;
-    else if (t_d >= kOverlapMinSeconds)
-      pl.cu_prefill_x256 = 384;
-    else
-      pl.cu_prefill_x256 = (int)std::max<int64_t>(1, std::min<int64_t>(256, 256LL * pl.p_tasks / lim.num_cus));
   } else {
     pl.share_num = pl.has_p ? 1 : 0;
     pl.share_den = 1;

@@ -23,8 +23,10 @@ enum { kPolicyCuBalanced = 0, kPolicyProportional = 1, kPolicyHalf = 2, kPolicyS
 
 constexpr int kPageSize = 16;
 constexpr int kWavesPerWG = 4;
-constexpr int kMaxSplitTokens = 1024;   // one lane per page id in a 64-lane wave
+constexpr int kSplitIdRegs = 4;         // page-id registers of a decode wave (64 ids each)
+constexpr int kMaxSplitTokens = 64 * kPageSize * kSplitIdRegs;  // 4096 tokens per decode wave task
 constexpr int kMinSplitTokens = 256;
+constexpr int kMaxContext = 1023 * kMinSplitTokens;  // 261888 tokens: <= 1023 decode splits per request
 constexpr int kMinPrefillSplitKeys = 1024;
 constexpr int kMaxSplitKeys = 16384;       // page ids of one split are staged in LDS
 constexpr int kShareDen = 64;
@@ -74,6 +76,8 @@ struct Plan {
   // decode
   bool has_d = false;
   int N = 0, T = 0, d_wave_tasks = 0, d_wg_tasks = 0;
+  int64_t d_total = 0;  // sum of decode contexts
+  int d_full = 0;       // decode units that are full T-token splits
   // fused scheduling
   int share_num = 0, share_den = 1, cu_prefill_x256 = 0, policy = 0;
 };

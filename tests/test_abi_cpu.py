@@ -95,7 +95,7 @@ def test_plan_invariants_on_configs(cid):
         assert st["prefill_tasks"] <= 2 * slots
     # decode: every (request, kv head) split into ceil(L / T) one-wave units
     T = st["decode_split_tokens"]
-    assert T % 16 == 0 and 256 <= T <= 1024
+    assert T % 16 == 0 and 256 <= T <= 4096
     assert st["decode_wave_tasks"] == hkv * sum(-(-int(L) // T) for L in lens)
     assert st["decode_wg_tasks"] == -(-st["decode_wave_tasks"] // 4)
     assert st["grid"] == st["prefill_tasks"] + st["decode_wg_tasks"]
@@ -153,7 +153,8 @@ def test_validation_null_pointers():
 
 @pytest.mark.parametrize("kw", [dict(head_dim=96), dict(num_q_heads=24, num_kv_heads=8),
                                 dict(page_size=8), dict(dtype=pod.POD_F32, head_dim=128),
-                                dict(num_q_heads=32, num_kv_heads=2), dict(wg_per_cu=4)])
+                                dict(num_q_heads=32, num_kv_heads=2), dict(wg_per_cu=4),
+                                dict(max_context=261889)])
 def test_unsupported_shapes(kw):
     cfg = _cfg(2, **kw)
     with pytest.raises(pod.PodAttnError) as e:
