@@ -36,7 +36,7 @@ class PodAttnConfig(ctypes.Structure):
                 ("max_context", ctypes.c_int32), ("max_total_context", ctypes.c_int64),
                 ("wg_per_cu", ctypes.c_int32), ("prefill_split_cap_waves", ctypes.c_int32),
                 ("policy", ctypes.c_int32), ("device", ctypes.c_int32),
-                ("prefill_slots_x256", ctypes.c_int32)]
+                ("prefill_slots_x256", ctypes.c_int32), ("decode_split_tokens", ctypes.c_int32)]
 
 
 class PodPrefillArgs(ctypes.Structure):
@@ -109,10 +109,12 @@ def status_string(status: int) -> str:
 def make_config(dtype=POD_BF16, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
                 sm_scale=0.0, max_chunk_len=4096, max_num_decode=256, max_context=32768,
                 max_total_context=0, wg_per_cu=0, prefill_split_cap_waves=0,
-                policy=POD_POLICY_CU_BALANCED, device=-1, prefill_slots_x256=0) -> PodAttnConfig:
+                policy=POD_POLICY_CU_BALANCED, device=-1, prefill_slots_x256=0,
+                decode_split_tokens=0) -> PodAttnConfig:
     return PodAttnConfig(dtype, num_q_heads, num_kv_heads, head_dim, page_size, sm_scale,
                          max_chunk_len, max_num_decode, max_context, max_total_context,
-                         wg_per_cu, prefill_split_cap_waves, policy, device, prefill_slots_x256)
+                         wg_per_cu, prefill_split_cap_waves, policy, device, prefill_slots_x256,
+                         decode_split_tokens)
 
 
 def _ptr(t) -> Optional[int]:

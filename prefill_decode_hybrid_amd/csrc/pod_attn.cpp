@@ -46,6 +46,10 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   if (c->prefill_split_cap_waves < 0) return POD_ERR_INVALID_ARG;
   if (c->policy < pod::kPolicyCuBalanced || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
   if (c->prefill_slots_x256 < 0 || c->prefill_slots_x256 > 2 * 256) return POD_ERR_INVALID_ARG;
+  if (c->decode_split_tokens != 0 &&
+      (c->decode_split_tokens % pod::kPageSize != 0 || c->decode_split_tokens < pod::kMinSplitTokens ||
+       c->decode_split_tokens > pod::kMaxSplitTokens))
+    return POD_ERR_INVALID_ARG;
   lim.max_chunk_len = c->max_chunk_len;
   lim.max_num_decode = c->max_num_decode;
   lim.max_context = c->max_context;
@@ -54,6 +58,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   lim.cap_waves = c->prefill_split_cap_waves ? c->prefill_split_cap_waves : 2;
   lim.policy = c->policy;
   lim.slots_x256 = c->prefill_slots_x256;
+  lim.split_tokens = c->decode_split_tokens;
   scale = c->sm_scale > 0.0f ? c->sm_scale : 1.0f / std::sqrt((float)s.d);
   return POD_OK;
 }

@@ -153,12 +153,17 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   // (prefill: its FLOPs at the tile's rate, or one task's duration if the
   // chunk has few tasks):
   //  * prefill longer: prefill takes every slot and decode fills its tail;
-  //  * prefill under 1/8 of decode: decode first, prefill fills the tail;
+  //  * prefill under 2/7 of decode: decode first, prefill fills the tail.
+  //    Decode streams KV at ~83% of the HBM peak on its own, so a short
+  //    prefill has little to hide behind; sharing the CUs with it slowed
+  //    the decode by more than the prefill took alone (measured on every
+  //    512-token chunk of a 16K prompt beside 64 16K decodes, and on
+  //    1024-token chunks up to offset 8K);
   //  * otherwise, a large batch: the roles overlap on every CU (the
   //    method's premise) with 1.5 prefill slots per CU on average -- a
   //    decode workgroup beside a prefill one streams at close to its full
-  //    rate while the prefill keeps its tail short (measured best from the
-  //    long-context batch down to late 512-token chunks of a 16K prompt
+  //    rate while the prefill keeps its tail short (measured best on the
+  //    long-context batch and on late 1024-token chunks of a 16K prompt
   //    beside 64 16K decodes);
   //  * otherwise (a small batch): as many prefill slots as prefill tasks,
   //    so every tile starts at once beside the decodes.
@@ -172,7 +177,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
       pl.cu_prefill_x256 = lim.slots_x256;
     else if (t_p >= t_d)
       pl.cu_prefill_x256 = 256 * lim.wg_per_cu;
-    else if (8.0 * t_p < t_d)
+    else if (3.5 * t_p < t_d)
       pl.cu_prefill_x256 = 0;
     else if (t_d >= kOverlapMinSeconds)
       pl.cu_prefill_x256 = 384;
@@ -196,6 +201,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     const int64_t target = (int64_t)lim.num_cus * 5;
     int64_t T = round_up(std::min(ceil_div(pl.d_total * s.hkv, target), median), kPageSize);
     T = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(kMinSplitTokens, T));
+    if (lim.split_tokens > 0) T = lim.split_tokens;
     pl.T = (int)T;
     int64_t units = 0, full = 0;
     for (int r = 0; r < d.N; ++r) {

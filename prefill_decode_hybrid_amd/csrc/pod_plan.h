@@ -50,6 +50,7 @@ struct Limits {
   int64_t max_total_context = 0;
   int wg_per_cu = 2, cap_waves = 2, policy = kPolicyCuBalanced;
   int slots_x256 = 0;  // prefill slots per CU for the CU-balanced policy; 0: from the batch
+  int split_tokens = 0;  // decode tokens per wave task; 0: from the batch
   int num_cus = 0;
   // capacities derived by workspace_layout()
   int64_t cap_prefill_tasks = 0, cap_wave_tasks = 0, cap_tiles = 0;

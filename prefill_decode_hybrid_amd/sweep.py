@@ -42,6 +42,8 @@ def main(argv=None):
     ap.add_argument("--policy", type=int, default=0)
     ap.add_argument("--slots-x256", type=int, default=0,
                     help="CU-balanced policy: prefill workgroups per CU in 1/256 (0: the planner's choice)")
+    ap.add_argument("--split-tokens", type=int, default=0,
+                    help="decode tokens per wave task (0: the planner's choice)")
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--seed", type=int, default=0)
@@ -65,7 +67,7 @@ def main(argv=None):
     dev = full.to("cuda:0")
     ctx_host = full.context_lens.clone().contiguous()
     cfg = pod.config_for_batch(full, policy=a.policy, prefill_split_cap_waves=a.split_cap,
-                               prefill_slots_x256=a.slots_x256)
+                               prefill_slots_x256=a.slots_x256, decode_split_tokens=a.split_tokens)
     att = pod.PodAttention(cfg)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
@@ -125,6 +127,7 @@ def main(argv=None):
         rows.append({"chunk": i, "offset": p0, "fused_us": round(med[0], 1), "serial_us": round(med[1], 1),
                      "two_stream_us": round(med[2], 1), "prefill_tasks": plan["prefill_tasks"],
                      "prefill_splits": plan["prefill_splits"], "cu_prefill_x256": plan["cu_prefill_x256"],
+                     "decode_split_tokens": plan["decode_split_tokens"],
                      "fused_equals_split": same})
         print(f"[sweep] chunk {i} @ {p0}: fused {med[0]:.1f} serial {med[1]:.1f} streams {med[2]:.1f} us "
               f"(splits {plan['prefill_splits']}, x256 {plan['cu_prefill_x256']})", file=sys.stderr, flush=True)
@@ -132,7 +135,7 @@ def main(argv=None):
     out = {"sweep": "chunked prefill beside a fixed decode batch", "prompt": a.prompt, "chunk": a.chunk,
            "num_decode": a.num_decode, "decode_context": a.decode_context, "heads": [a.num_q_heads, a.num_kv_heads],
            "head_dim": a.head_dim, "chunks_timed": len(rows), "split_cap_waves": a.split_cap or 2,
-           "policy": a.policy, "slots_x256": a.slots_x256, "steps": a.steps, "totals": tot,
+           "policy": a.policy, "slots_x256": a.slots_x256, "split_tokens": a.split_tokens, "steps": a.steps, "totals": tot,
            "speedup_vs_serial": round(tot["serial_us"] / tot["fused_us"], 4),
            "speedup_vs_two_stream": round(tot["two_stream_us"] / tot["fused_us"], 4),
            "fused_equals_split": all_same, "chunks": rows}

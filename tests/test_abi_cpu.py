@@ -119,6 +119,37 @@ def test_split_cap_limits_prefill_tasks():
     assert st["prefill_tasks"] <= 1 * 256 * st["wg_per_cu"]
 
 
+def test_forced_decode_split_tokens():
+    lens = [5000, 300, 16384]
+    for T in (256, 1024, 4096):
+        st = plan(_cfg(3, decode_split_tokens=T), pod.MODE_HYBRID, _prefill(512, 1024), _decode(lens))
+        assert st["decode_split_tokens"] == T
+        assert st["decode_wave_tasks"] == 8 * sum(-(-L // T) for L in lens)
+    for bad in (100, 255, 4112, 1000, -16):
+        with pytest.raises(pod.PodAttnError) as e:
+            plan(_cfg(3, decode_split_tokens=bad), pod.MODE_DECODE, None, _decode(lens))
+        assert e.value.status == pod.POD_ERR_INVALID_ARG
+
+
+def test_decode_split_is_the_same_in_every_mode():
+    # the split depends on the decode batch alone, so decode results match bit for bit
+    lens = inputs.draw_context_lens(4, 0)
+    cfg = _cfg(4)
+    a = plan(cfg, pod.MODE_HYBRID, _prefill(256, 2048), _decode(lens))
+    b = plan(cfg, pod.MODE_DECODE, None, _decode(lens))
+    assert a["decode_split_tokens"] == b["decode_split_tokens"]
+    assert a["decode_wave_tasks"] == b["decode_wave_tasks"]
+
+
+@pytest.mark.parametrize("P0,x", [(0, 0), (4096, 0), (15872, 0), (15360, 384)])
+def test_role_mix_by_work_ratio(P0, x):
+    # 64 decodes of 16K beside one chunk of a 16K prompt: a short chunk runs
+    # after the decodes, a long one overlaps them on every CU
+    C = 1024 if P0 == 15360 else 512
+    st = plan(_cfg(3), pod.MODE_HYBRID, _prefill(C, P0), _decode([16384] * 64))
+    assert st["cu_prefill_x256"] == x
+
+
 @pytest.mark.parametrize("bad,code", [
     (dict(prefill=(0, 0)), pod.POD_ERR_INVALID_ARG),       # empty chunk
     (dict(prefill=(8, -1)), pod.POD_ERR_INVALID_ARG),      # negative offset
