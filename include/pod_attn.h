@@ -2,7 +2,8 @@
  * pod_attn.h -- C ABI of the hybrid-batch attention library (gfx950).
  *
  * One call computes exact softmax attention for a hybrid batch: one causal
- * chunked-prefill request plus many single-token decode requests over a
+ * chunked-prefill request (or, through the _varlen calls, up to
+ * POD_MAX_CHUNKS of them) plus many single-token decode requests over a
  * paged grouped-query KV cache.  The batch shape is the one POD-Attention is
  * built for (paper §2.1: a hybrid batch commonly holds one prefill chunk and
  * several decodes; §3: both sets of inputs reach one attention call), and
@@ -92,7 +93,7 @@ typedef struct {
     int32_t head_dim;         /* 64 or 128 (POD_F32: 64 only)                          */
     int32_t page_size;        /* 16                                                    */
     float sm_scale;           /* softmax scale; 0 selects 1/sqrt(head_dim)             */
-    int32_t max_chunk_len;    /* largest prefill chunk a call may pass                 */
+    int32_t max_chunk_len;    /* most prefill rows a call may pass (all chunks)        */
     int32_t max_num_decode;   /* largest decode batch                                  */
     int32_t max_context;      /* largest decode context and largest offset+chunk;
                                  at most 261888 (POD_ERR_UNSUPPORTED above)            */
@@ -129,6 +130,25 @@ typedef struct {
     int32_t num_decode;         /* >= 1                                                */
 } pod_decode_args;
 
+/* Several prefill chunks in one call.  The paper's hybrid batch commonly
+ * holds one chunk (§2.1); a scheduler that packs chunks of several prompts
+ * passes them here.  Chunk c is its own request: rows row_c .. row_c +
+ * chunk_lens[c] - 1 of q and o, where row_c is the sum of the earlier chunk
+ * lengths, row i of it at absolute position chunk_offsets[c] + i seeing keys
+ * 0 .. chunk_offsets[c] + i of its own page table (row c of page_table).
+ * The sum of the chunk lengths must not exceed max_chunk_len of the config.
+ * With one chunk the result equals pod_attn_hybrid's bit for bit. */
+#define POD_MAX_CHUNKS 16
+typedef struct {
+    const void *q;              /* device [sum of chunk_lens, Hq, head_dim]            */
+    void *o;                    /* device [sum of chunk_lens, Hq, head_dim]            */
+    const int32_t *page_table;  /* device [num_chunks, page_table_stride]              */
+    int32_t page_table_stride;  /* >= ceil((chunk_offset+chunk_len)/page_size) of every chunk */
+    const int32_t *chunk_lens_host;    /* host [num_chunks], each >= 1                 */
+    const int32_t *chunk_offsets_host; /* host [num_chunks], each >= 0                 */
+    int32_t num_chunks;         /* 1 .. POD_MAX_CHUNKS                                 */
+} pod_prefill_batch;
+
 /* What the last call (or pod_attn_plan) decided; the runtime report the
  * Silicon & Systems digest asks for ("Isolation and predictability"):
  * the virtual-workgroup mix, tile choices and the reason for a fallback. */
@@ -141,9 +161,10 @@ typedef struct {
     int32_t grid;               /* workgroups launched                                 */
     int32_t prefill_rows_per_tile, prefill_heads_per_tile;
     int32_t prefill_tiles;      /* (row block, kv head, head group) tiles              */
-    int32_t prefill_splits;     /* KV splits per tile                                  */
-    int32_t prefill_split_keys; /* keys per split                                      */
-    int32_t prefill_tasks;      /* tiles * splits (prefill workgroups)                 */
+    int32_t prefill_splits;     /* KV splits per tile (of the first chunk in task order,
+                                   the one with the longest key range)                */
+    int32_t prefill_split_keys; /* keys per split (same chunk)                         */
+    int32_t prefill_tasks;      /* tiles * splits over all chunks (prefill workgroups) */
     int32_t decode_split_tokens;/* tokens per decode wave task                         */
     int32_t decode_wave_tasks;  /* (request, kv head, token split) units, one wave each */
     int32_t decode_wg_tasks;    /* decode workgroups (4 wave tasks each)               */
@@ -151,6 +172,7 @@ typedef struct {
     int32_t cu_prefill_x256;    /* CU-balanced policy: prefill workgroups kept per CU,
                                    averaged over CUs, in 1/256                        */
     int32_t policy;
+    int32_t prefill_chunks;     /* prefill chunks of the call (0 without prefill)     */
 } pod_attn_stats;
 
 /* Validate `cfg`, pick the device, reserve the workspace.  Returns POD_OK and
@@ -173,6 +195,21 @@ int pod_attn_prefill_only(pod_attn_handle *h, const void *k_pool, const void *v_
 /* Decode half only (the bandwidth-bound baseline kernel). */
 int pod_attn_decode_only(pod_attn_handle *h, const void *k_pool, const void *v_pool,
                          int64_t num_pages, const pod_decode_args *decode, pod_stream_t stream);
+
+/* The same three calls with several prefill chunks (pod_prefill_batch).
+ * Chunks run longest key range first; their tiles share the launch like
+ * the tiles of one chunk.  Errors as above, and POD_ERR_INVALID_ARG for
+ * num_chunks outside 1 .. POD_MAX_CHUNKS, a page_table_stride below a
+ * chunk's page count, or chunk lengths summing above max_chunk_len. */
+int pod_attn_hybrid_varlen(pod_attn_handle *h, const void *k_pool, const void *v_pool,
+                           int64_t num_pages, const pod_prefill_batch *prefill,
+                           const pod_decode_args *decode, pod_stream_t stream);
+int pod_attn_prefill_only_varlen(pod_attn_handle *h, const void *k_pool, const void *v_pool,
+                                 int64_t num_pages, const pod_prefill_batch *prefill,
+                                 pod_stream_t stream);
+int pod_attn_plan_varlen(const pod_attn_config *cfg, int32_t num_cus, int32_t mode,
+                         const pod_prefill_batch *prefill, const pod_decode_args *decode,
+                         pod_attn_stats *out);
 
 /* Copy the plan of the last successful compute call into *out. */
 int pod_attn_get_stats(const pod_attn_handle *h, pod_attn_stats *out);

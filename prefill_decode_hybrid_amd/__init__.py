@@ -23,8 +23,11 @@ POD_BF16, POD_F32 = 0, 1
 POD_POLICY_CU_BALANCED, POD_POLICY_PROPORTIONAL, POD_POLICY_HALF, POD_POLICY_STATIC = 0, 1, 2, 3
 MODE_HYBRID, MODE_PREFILL, MODE_DECODE = 0, 1, 2
 
+POD_MAX_CHUNKS = 16
+
 EXPORTED = ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_prefill_only",
-            "pod_attn_decode_only", "pod_attn_get_stats", "pod_attn_plan",
+            "pod_attn_decode_only", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
+            "pod_attn_get_stats", "pod_attn_plan", "pod_attn_plan_varlen",
             "pod_attn_status_string", "pod_attn_last_error")
 
 
@@ -50,12 +53,18 @@ class PodDecodeArgs(ctypes.Structure):
                 ("context_lens_host", ctypes.c_void_p), ("num_decode", ctypes.c_int32)]
 
 
+class PodPrefillBatch(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("o", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("page_table_stride", ctypes.c_int32), ("chunk_lens_host", ctypes.c_void_p),
+                ("chunk_offsets_host", ctypes.c_void_p), ("num_chunks", ctypes.c_int32)]
+
+
 class PodAttnStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "fallback", "num_cus", "wg_per_cu", "grid", "prefill_rows_per_tile",
         "prefill_heads_per_tile", "prefill_tiles", "prefill_splits", "prefill_split_keys",
         "prefill_tasks", "decode_split_tokens", "decode_wave_tasks", "decode_wg_tasks",
-        "share_num", "share_den", "cu_prefill_x256", "policy")]
+        "share_num", "share_den", "cu_prefill_x256", "policy", "prefill_chunks")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -85,6 +94,11 @@ def load(path: str = LIB_PATH):
                                     ctypes.POINTER(PodDecodeArgs), P]
     lib.pod_attn_prefill_only.argtypes = [P, P, P, i64, ctypes.POINTER(PodPrefillArgs), P]
     lib.pod_attn_decode_only.argtypes = [P, P, P, i64, ctypes.POINTER(PodDecodeArgs), P]
+    lib.pod_attn_hybrid_varlen.argtypes = [P, P, P, i64, ctypes.POINTER(PodPrefillBatch),
+                                           ctypes.POINTER(PodDecodeArgs), P]
+    lib.pod_attn_prefill_only_varlen.argtypes = [P, P, P, i64, ctypes.POINTER(PodPrefillBatch), P]
+    lib.pod_attn_plan_varlen.argtypes = [ctypes.POINTER(PodAttnConfig), i32, i32, ctypes.POINTER(PodPrefillBatch),
+                                         ctypes.POINTER(PodDecodeArgs), ctypes.POINTER(PodAttnStats)]
     lib.pod_attn_get_stats.argtypes = [P, ctypes.POINTER(PodAttnStats)]
     lib.pod_attn_plan.argtypes = [ctypes.POINTER(PodAttnConfig), i32, i32, ctypes.POINTER(PodPrefillArgs),
                                   ctypes.POINTER(PodDecodeArgs), ctypes.POINTER(PodAttnStats)]
@@ -93,7 +107,8 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_last_error.argtypes = [P]
     lib.pod_attn_last_error.restype = ctypes.c_char_p
     for name in ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_prefill_only",
-                 "pod_attn_decode_only", "pod_attn_get_stats", "pod_attn_plan"):
+                 "pod_attn_decode_only", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
+                 "pod_attn_get_stats", "pod_attn_plan", "pod_attn_plan_varlen"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -123,6 +138,17 @@ def _ptr(t) -> Optional[int]:
 
 def prefill_args(q, o, page_table, chunk_offset: int) -> PodPrefillArgs:
     return PodPrefillArgs(_ptr(q), _ptr(o), _ptr(page_table), int(q.shape[0]), int(chunk_offset))
+
+
+def prefill_batch(q, o, page_table, chunks) -> PodPrefillBatch:
+    """chunks: [(chunk_len, chunk_offset)] in row order; page_table: device int32 [n, stride]."""
+    import numpy as np
+    lens = np.ascontiguousarray([c for c, _ in chunks], dtype=np.int32)
+    offs = np.ascontiguousarray([p for _, p in chunks], dtype=np.int32)
+    a = PodPrefillBatch(_ptr(q), _ptr(o), _ptr(page_table), int(page_table.shape[1]), lens.ctypes.data,
+                        offs.ctypes.data, len(chunks))
+    a._keep = (lens, offs)  # the host arrays live as long as the struct
+    return a
 
 
 def decode_args(q, o, page_table, context_lens, context_lens_host) -> PodDecodeArgs:
@@ -181,6 +207,20 @@ def pod_attn_decode_only(h, k_pool, v_pool, decode: PodDecodeArgs, stream=None) 
     _check(h, rc, "pod_attn_decode_only")
 
 
+def pod_attn_hybrid_varlen(h, k_pool, v_pool, prefill: Optional[PodPrefillBatch],
+                           decode: Optional[PodDecodeArgs], stream=None) -> None:
+    rc = load().pod_attn_hybrid_varlen(h, _ptr(k_pool), _ptr(v_pool), int(k_pool.shape[0]),
+                                       ctypes.byref(prefill) if prefill is not None else None,
+                                       ctypes.byref(decode) if decode is not None else None, _stream_ptr(stream))
+    _check(h, rc, "pod_attn_hybrid_varlen")
+
+
+def pod_attn_prefill_only_varlen(h, k_pool, v_pool, prefill: PodPrefillBatch, stream=None) -> None:
+    rc = load().pod_attn_prefill_only_varlen(h, _ptr(k_pool), _ptr(v_pool), int(k_pool.shape[0]),
+                                             ctypes.byref(prefill), _stream_ptr(stream))
+    _check(h, rc, "pod_attn_prefill_only_varlen")
+
+
 def pod_attn_get_stats(h) -> dict:
     st = PodAttnStats()
     _check(h, load().pod_attn_get_stats(h, ctypes.byref(st)), "pod_attn_get_stats")
@@ -195,6 +235,17 @@ def pod_attn_plan(cfg: PodAttnConfig, num_cus: int, mode: int, prefill=None, dec
                               ctypes.byref(decode) if decode is not None else None, ctypes.byref(st))
     if rc != POD_OK:
         raise PodAttnError(rc, "pod_attn_plan")
+    return st.as_dict()
+
+
+def pod_attn_plan_varlen(cfg: PodAttnConfig, num_cus: int, mode: int, prefill=None, decode=None) -> dict:
+    """Host-only plan of a several-chunk call (no GPU needed)."""
+    st = PodAttnStats()
+    rc = load().pod_attn_plan_varlen(ctypes.byref(cfg), int(num_cus), int(mode),
+                                     ctypes.byref(prefill) if prefill is not None else None,
+                                     ctypes.byref(decode) if decode is not None else None, ctypes.byref(st))
+    if rc != POD_OK:
+        raise PodAttnError(rc, "pod_attn_plan_varlen")
     return st.as_dict()
 
 
@@ -237,6 +288,18 @@ class PodAttention:
         _, da = self.args(batch, None, o_decode, ctx_host)
         pod_attn_decode_only(self.h, batch.k_pool, batch.v_pool, da, stream)
 
+    # several prefill chunks (batch.chunks set, page_table_prefill [n, stride])
+    def hybrid_varlen(self, batch, o_prefill, o_decode, ctx_host, stream=None):
+        _, da = self.args(batch, None, o_decode, ctx_host)
+        pa = None
+        if batch.q_prefill is not None and o_prefill is not None:
+            pa = prefill_batch(batch.q_prefill, o_prefill, batch.page_table_prefill, batch.chunk_list())
+        pod_attn_hybrid_varlen(self.h, batch.k_pool, batch.v_pool, pa, da, stream)
+
+    def prefill_only_varlen(self, batch, o_prefill, stream=None):
+        pa = prefill_batch(batch.q_prefill, o_prefill, batch.page_table_prefill, batch.chunk_list())
+        pod_attn_prefill_only_varlen(self.h, batch.k_pool, batch.v_pool, pa, stream)
+
     def stats(self) -> dict:
         return pod_attn_get_stats(self.h)
 
@@ -244,7 +307,7 @@ class PodAttention:
 def config_for_batch(batch, **kw) -> PodAttnConfig:
     """A config whose limits fit `batch` (a HybridBatch from .inputs)."""
     lens = [] if batch.context_lens is None else batch.context_lens.tolist()
-    lp = batch.chunk_offset + batch.chunk_len
+    lp = max([c + p for c, p in batch.chunk_list()] + [0])
     return make_config(
         dtype=POD_BF16 if batch.spec["dtype"] == "bf16" else POD_F32,
         num_q_heads=batch.num_q_heads, num_kv_heads=batch.num_kv_heads, head_dim=batch.head_dim,

@@ -12,6 +12,8 @@
 #include "pod_launch.h"
 #include "pod_plan.h"
 
+static_assert(POD_MAX_CHUNKS == pod::kMaxChunks, "chunk limit of the ABI and the planner");
+
 struct pod_attn_handle {
   pod::Shape shape;
   pod::Limits lim;
@@ -73,8 +75,9 @@ void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
   st->prefill_rows_per_tile = pl.rows_per_tile;
   st->prefill_heads_per_tile = pl.heads_per_tile;
   st->prefill_tiles = pl.tiles;
-  st->prefill_splits = pl.splits;
-  st->prefill_split_keys = pl.split_keys;
+  st->prefill_chunks = pl.has_p ? pl.n_chunks : 0;
+  st->prefill_splits = pl.has_p ? pl.ch[0].splits : 0;
+  st->prefill_split_keys = pl.has_p ? pl.ch[0].split_keys : 0;
   st->prefill_tasks = pl.has_p ? pl.p_tasks : 0;
   st->decode_split_tokens = pl.T;
   st->decode_wave_tasks = pl.has_d ? pl.d_wave_tasks : 0;
@@ -90,14 +93,43 @@ int hip_fail(pod_attn_handle* h, hipError_t e, const char* what) {
   return POD_ERR_HIP;
 }
 
-pod::PrefillIn prefill_in(const pod_prefill_args* a) {
-  pod::PrefillIn p;
-  if (a) {
-    p.present = true;
-    p.C = a->chunk_len;
-    p.P0 = a->chunk_offset;
+// The prefill half of a call: device buffers plus the chunk shapes.
+struct PrefillView {
+  const void* q = nullptr;
+  void* o = nullptr;
+  const int32_t* pt = nullptr;
+  pod::PrefillIn in;
+};
+
+int prefill_one(const pod_prefill_args* a, PrefillView& v) {
+  if (!a) return POD_OK;
+  if (!a->q || !a->o || !a->page_table) return POD_ERR_INVALID_ARG;
+  v.q = a->q;
+  v.o = a->o;
+  v.pt = a->page_table;
+  v.in.present = true;
+  v.in.n = 1;
+  v.in.C[0] = a->chunk_len;
+  v.in.P0[0] = a->chunk_offset;
+  return POD_OK;
+}
+
+int prefill_many(const pod_prefill_batch* b, PrefillView& v) {
+  if (!b) return POD_OK;
+  if (!b->q || !b->o || !b->page_table || !b->chunk_lens_host || !b->chunk_offsets_host)
+    return POD_ERR_INVALID_ARG;
+  if (b->num_chunks < 1 || b->num_chunks > POD_MAX_CHUNKS || b->page_table_stride < 1) return POD_ERR_INVALID_ARG;
+  v.q = b->q;
+  v.o = b->o;
+  v.pt = b->page_table;
+  v.in.present = true;
+  v.in.n = b->num_chunks;
+  v.in.stride = b->page_table_stride;
+  for (int c = 0; c < b->num_chunks; ++c) {
+    v.in.C[c] = b->chunk_lens_host[c];
+    v.in.P0[c] = b->chunk_offsets_host[c];
   }
-  return p;
+  return POD_OK;
 }
 
 pod::DecodeIn decode_in(const pod_decode_args* a) {
@@ -111,20 +143,19 @@ pod::DecodeIn decode_in(const pod_decode_args* a) {
   return d;
 }
 
-int check_pointers(const pod_prefill_args* p, const pod_decode_args* d) {
-  if (p && (!p->q || !p->o || !p->page_table)) return POD_ERR_INVALID_ARG;
+int check_decode(const pod_decode_args* d) {
   if (d && (!d->q || !d->o || !d->page_table || !d->context_lens || !d->context_lens_host))
     return POD_ERR_INVALID_ARG;
   return POD_OK;
 }
 
 int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, int64_t num_pages,
-        const pod_prefill_args* pa, const pod_decode_args* da, pod_stream_t stream) {
+        const PrefillView& pv, const pod_decode_args* da, pod_stream_t stream) {
   if (!h || !k_pool || !v_pool || num_pages < 1 || num_pages > 0xffffffffLL) return POD_ERR_INVALID_ARG;
-  int rc = check_pointers(pa, da);
+  int rc = check_decode(da);
   if (rc) return rc;
   pod::Plan pl;
-  rc = pod::make_plan(h->shape, h->lim, mode, prefill_in(pa), decode_in(da), &pl);
+  rc = pod::make_plan(h->shape, h->lim, mode, pv.in, decode_in(da), &pl);
   if (rc) return rc;
 
   const pod::Shape& s = h->shape;
@@ -144,20 +175,19 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
   p.p_part = reinterpret_cast<float*>(h->ws + h->lay.p_part);
   p.d_part = reinterpret_cast<float*>(h->ws + h->lay.d_part);
   if (pl.has_p) {
-    p.qp = pa->q;
-    p.op = pa->o;
-    p.pt_p = pa->page_table;
-    p.C = pl.C;
-    p.P0 = pl.P0;
-    p.Lp = pl.Lp;
+    p.qp = pv.q;
+    p.op = pv.o;
+    p.pt_p = pv.pt;
     p.rows_per_tile = pl.rows_per_tile;
     p.heads_per_tile = pl.heads_per_tile;
-    p.row_blocks = pl.row_blocks;
     p.head_groups = pl.head_groups;
-    p.tiles = pl.tiles;
-    p.splits = pl.splits;
-    p.split_keys = pl.split_keys;
     p.p_tasks = pl.p_tasks;
+    p.n_chunks = pl.n_chunks;
+    for (int k = 0; k < pl.n_chunks; ++k) {
+      const pod::ChunkPlan& c = pl.ch[k];
+      p.ch[k] = pod::PfChunk{c.task_base, c.tile_base, c.row_base, c.src * pl.stride,
+                             c.C, c.P0, c.splits, c.split_keys, c.row_blocks};
+    }
   }
   if (pl.has_d) {
     p.qd = da->q;
@@ -190,6 +220,25 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
     if (which == pod::kKernelHybrid) ++h->fused_launches;  // the next one runs on the cleared block
   }
   fill_stats(pl, &h->stats);
+  return POD_OK;
+}
+
+int plan_only(const pod_attn_config* cfg, int32_t num_cus, int32_t mode, const PrefillView& pv,
+              const pod_decode_args* decode, pod_attn_stats* out) {
+  if (!out || num_cus < 1 || mode < 0 || mode > 2) return POD_ERR_INVALID_ARG;
+  pod::Shape s;
+  pod::Limits lim;
+  float scale = 0.0f;
+  int rc = validate_config(cfg, s, lim, scale);
+  if (rc) return rc;
+  rc = check_decode(decode);
+  if (rc) return rc;
+  lim.num_cus = num_cus;
+  pod::derive_capacities(s, lim);
+  pod::Plan pl;
+  rc = pod::make_plan(s, lim, mode, pv.in, decode_in(decode), &pl);
+  if (rc) return rc;
+  fill_stats(pl, out);
   return POD_OK;
 }
 
@@ -256,19 +305,38 @@ int pod_attn_destroy(pod_attn_handle* h) {
 
 int pod_attn_hybrid(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,
                     const pod_prefill_args* prefill, const pod_decode_args* decode, pod_stream_t stream) {
-  return run(h, pod::kModeHybrid, k_pool, v_pool, num_pages, prefill, decode, stream);
+  PrefillView pv;
+  const int rc = prefill_one(prefill, pv);
+  return rc ? rc : run(h, pod::kModeHybrid, k_pool, v_pool, num_pages, pv, decode, stream);
 }
 
 int pod_attn_prefill_only(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,
                           const pod_prefill_args* prefill, pod_stream_t stream) {
   if (!prefill) return POD_ERR_INVALID_ARG;
-  return run(h, pod::kModePrefill, k_pool, v_pool, num_pages, prefill, nullptr, stream);
+  PrefillView pv;
+  const int rc = prefill_one(prefill, pv);
+  return rc ? rc : run(h, pod::kModePrefill, k_pool, v_pool, num_pages, pv, nullptr, stream);
 }
 
 int pod_attn_decode_only(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,
                          const pod_decode_args* decode, pod_stream_t stream) {
   if (!decode) return POD_ERR_INVALID_ARG;
-  return run(h, pod::kModeDecode, k_pool, v_pool, num_pages, nullptr, decode, stream);
+  return run(h, pod::kModeDecode, k_pool, v_pool, num_pages, PrefillView{}, decode, stream);
+}
+
+int pod_attn_hybrid_varlen(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,
+                           const pod_prefill_batch* prefill, const pod_decode_args* decode, pod_stream_t stream) {
+  PrefillView pv;
+  const int rc = prefill_many(prefill, pv);
+  return rc ? rc : run(h, pod::kModeHybrid, k_pool, v_pool, num_pages, pv, decode, stream);
+}
+
+int pod_attn_prefill_only_varlen(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,
+                                 const pod_prefill_batch* prefill, pod_stream_t stream) {
+  if (!prefill) return POD_ERR_INVALID_ARG;
+  PrefillView pv;
+  const int rc = prefill_many(prefill, pv);
+  return rc ? rc : run(h, pod::kModePrefill, k_pool, v_pool, num_pages, pv, nullptr, stream);
 }
 
 int pod_attn_get_stats(const pod_attn_handle* h, pod_attn_stats* out) {
@@ -279,21 +347,16 @@ int pod_attn_get_stats(const pod_attn_handle* h, pod_attn_stats* out) {
 
 int pod_attn_plan(const pod_attn_config* cfg, int32_t num_cus, int32_t mode, const pod_prefill_args* prefill,
                   const pod_decode_args* decode, pod_attn_stats* out) {
-  if (!out || num_cus < 1 || mode < 0 || mode > 2) return POD_ERR_INVALID_ARG;
-  pod::Shape s;
-  pod::Limits lim;
-  float scale = 0.0f;
-  int rc = validate_config(cfg, s, lim, scale);
-  if (rc) return rc;
-  rc = check_pointers(prefill, decode);
-  if (rc) return rc;
-  lim.num_cus = num_cus;
-  pod::derive_capacities(s, lim);
-  pod::Plan pl;
-  rc = pod::make_plan(s, lim, mode, prefill_in(prefill), decode_in(decode), &pl);
-  if (rc) return rc;
-  fill_stats(pl, out);
-  return POD_OK;
+  PrefillView pv;
+  const int rc = prefill_one(prefill, pv);
+  return rc ? rc : plan_only(cfg, num_cus, mode, pv, decode, out);
+}
+
+int pod_attn_plan_varlen(const pod_attn_config* cfg, int32_t num_cus, int32_t mode,
+                         const pod_prefill_batch* prefill, const pod_decode_args* decode, pod_attn_stats* out) {
+  PrefillView pv;
+  const int rc = prefill_many(prefill, pv);
+  return rc ? rc : plan_only(cfg, num_cus, mode, pv, decode, out);
 }
 
 const char* pod_attn_status_string(int status) {

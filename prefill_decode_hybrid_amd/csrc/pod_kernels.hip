@@ -19,6 +19,7 @@
 // computes O = sum_j softmax_j(scale * q.K_j) V_j over the visible keys.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 
 #include "pod_launch.h"
@@ -842,44 +843,85 @@ DEV void decode_wg(const PodParams& p, int wg_task, const LdsBufs& lb) {
 }
 
 // ---------------------------------------------------------- prefill (a2, a4)
-// A prefill task is (tile, KV split).  A tile is (row block, kv head g, head
-// group): 4 waves, wave w takes 32 (bf16) or 64 (fp32) consecutive chunk
-// rows of one query head of g.  K/V blocks of the split's key range are
-// staged once in LDS and shared by the 4 waves (the GQA heads of one kv
-// head reuse the same keys).
+// A prefill task is (chunk, tile, KV split).  A tile is (row block, kv head
+// g, head group): 4 waves, wave w takes 32 (bf16) or 64 (fp32) consecutive
+// chunk rows of one query head of g.  K/V blocks of the split's key range
+// are staged once in LDS and shared by the 4 waves (the GQA heads of one kv
+// head reuse the same keys).  Rows are chunk-local: row i of the chunk sits
+// at absolute position P0 + i and at row row_base + i of the packed q and o.
 struct TaskGeom {
+  int C, P0, Lp;      // the chunk: rows, offset, keys
+  int splits, tiles;  // the chunk's splits per tile and tiles
+  int row_base;       // the chunk's first row in q and o
+  const int32_t* pt;  // the chunk's page table
   int tile, split, rb, g, hg;
   int head, row0;     // this wave's head and first row
   int k0, k1;         // split key range, clipped to the tile's causal end
   int kw;             // this wave's last visible key + 1 within the split
 };
 
+typedef __attribute__((address_space(4))) const char karg_char_t;
+typedef __attribute__((address_space(4))) const PfChunk karg_chunk_t;
+
+// Chunk c of the launch, read from the kernel-argument segment with a
+// uniform index (a scalar load; indexing the by-value parameter would copy
+// the table to scratch).  The parameter block is the kernels' only argument.
+DEV PfChunk load_chunk(int c) {
+  karg_chunk_t* t =
+      (karg_chunk_t*)((karg_char_t*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(PodParams, ch)) + c;
+  PfChunk r;
+  r.task_base = t->task_base;
+  r.tile_base = t->tile_base;
+  r.row_base = t->row_base;
+  r.pt_base = t->pt_base;
+  r.C = t->C;
+  r.P0 = t->P0;
+  r.splits = t->splits;
+  r.split_keys = t->split_keys;
+  r.row_blocks = t->row_blocks;
+  return r;
+}
+
 template <int RPW>
 DEV TaskGeom prefill_geom(const PodParams& p, int task) {
   TaskGeom t;
-  int i = task;
+  task = __builtin_amdgcn_readfirstlane(task);
+  int c = 0;  // the last chunk whose first task is <= task
+#pragma unroll
+  for (int k = 1; k < kMaxChunks; ++k)
+    if (k < p.n_chunks && task >= p.ch[k].task_base) c = k;
+  const PfChunk ch = load_chunk(c);
+  t.C = ch.C;
+  t.P0 = ch.P0;
+  t.Lp = ch.C + ch.P0;
+  t.splits = ch.splits;
+  t.tiles = ch.row_blocks * p.head_groups * p.hkv;
+  t.row_base = ch.row_base;
+  t.pt = p.pt_p + ch.pt_base;
+  int i = task - ch.task_base;
   t.g = i % p.hkv;
   i /= p.hkv;
   t.hg = i % p.head_groups;
   i /= p.head_groups;
-  const int rbi = i % p.row_blocks;
-  t.split = i / p.row_blocks;
-  t.rb = p.row_blocks - 1 - rbi;  // longest (latest) row blocks first
-  t.tile = (t.rb * p.head_groups + t.hg) * p.hkv + t.g;
+  const int rbi = i % ch.row_blocks;
+  t.split = i / ch.row_blocks;
+  t.rb = ch.row_blocks - 1 - rbi;  // longest (latest) row blocks first
+  t.tile = ch.tile_base + (t.rb * p.head_groups + t.hg) * p.hkv + t.g;
   const int w = wave_id();
   const int G = p.hq / p.hkv;
   t.head = t.g * G + t.hg * p.heads_per_tile + (w % p.heads_per_tile);
   t.row0 = t.rb * p.rows_per_tile + (w / p.heads_per_tile) * RPW;
-  const int tile_end = p.P0 + min(p.C, (t.rb + 1) * p.rows_per_tile);  // causal end of the tile
-  t.k0 = t.split * p.split_keys;
-  t.k1 = min(t.k0 + p.split_keys, tile_end);
-  t.kw = min(t.k1, p.P0 + min(p.C, t.row0 + RPW));
+  const int tile_end = t.P0 + min(t.C, (t.rb + 1) * p.rows_per_tile);  // causal end of the tile
+  t.k0 = t.split * ch.split_keys;
+  t.k1 = min(t.k0 + ch.split_keys, tile_end);
+  t.kw = min(t.k1, t.P0 + min(t.C, t.row0 + RPW));
   return t;
 }
 
-// Copy the physical ids of pages [pg0, pg0 + n) into LDS (clamped into the pool).
-DEV void preload_page_ids(const PodParams& p, int pg0, int n, int* pids) {
-  for (int i = threadIdx.x; i < n; i += 256) pids[i] = (int)min((uint32_t)p.pt_p[pg0 + i], p.num_pages - 1u);
+// Copy the physical ids of pages [pg0, pg0 + n) of a page table into LDS
+// (clamped into the pool).
+DEV void preload_page_ids(const int32_t* pt, uint32_t num_pages, int pg0, int n, int* pids) {
+  for (int i = threadIdx.x; i < n; i += 256) pids[i] = (int)min((uint32_t)pt[pg0 + i], num_pages - 1u);
 }
 
 // Wait until at most N of this wave's vector memory operations are in flight
@@ -1006,18 +1048,18 @@ template <class E, int D, int RPW>
 DEV void prefill_finish_split(const PodParams& p, const TaskGeom& t, int task, const LdsBufs& lb) {
   wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) *lb.flag = atomicAdd(p.p_cnt + t.tile, 1u) == (uint32_t)p.splits - 1u;
+  if (threadIdx.x == 0) *lb.flag = atomicAdd(p.p_cnt + t.tile, 1u) == (uint32_t)t.splits - 1u;
   __syncthreads();
   if (!*lb.flag) return;
   const int w = wave_id();
   using Rc = PfRec<D, RPW>;
   // Tasks of one tile differ only in their split: task = split * tiles + (tile
   // position), so split s of this tile is task - (split - s) * tiles.
-  const char* part0 = reinterpret_cast<const char*>(p.p_part) + (int64_t)(task - t.split * p.tiles) * Rc::BYTES;
-  char* out0 = reinterpret_cast<char*>(p.op) + ((int64_t)t.row0 * p.hq + t.head) * D * E::bytes;
+  const char* part0 = reinterpret_cast<const char*>(p.p_part) + (int64_t)(task - t.split * t.tiles) * Rc::BYTES;
+  char* out0 = reinterpret_cast<char*>(p.op) + ((int64_t)(t.row_base + t.row0) * p.hq + t.head) * D * E::bytes;
   float* wl = reinterpret_cast<float*>(w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3]);
-  merge_rows<E, RPW, D, 16>(part0, (int64_t)p.tiles * Rc::BYTES, Rc::acc_off(w), Rc::m_off(w), Rc::l_off(w), p.splits,
-                        min(RPW, p.C - t.row0), out0, (int64_t)p.hq * D, wl);
+  merge_rows<E, RPW, D, 16>(part0, (int64_t)t.tiles * Rc::BYTES, Rc::acc_off(w), Rc::m_off(w), Rc::l_off(w), t.splits,
+                        min(RPW, t.C - t.row0), out0, (int64_t)p.hq * D, wl);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(p.p_cnt + t.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1039,11 +1081,12 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
   // Q^T operand: lane holds d = 16 ks + 8 half .. +8 of its row
   bf16x8_t qf[KS];
   {
-    const char* qrow = reinterpret_cast<const char*>(p.qp) + (((int64_t)row * p.hq + t.head) * D + 8 * half) * 2;
+    const char* qrow =
+        reinterpret_cast<const char*>(p.qp) + (((int64_t)(t.row_base + row) * p.hq + t.head) * D + 8 * half) * 2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < p.C) v = *reinterpret_cast<const uint4*>(qrow + ks * 32);
+      if (row < t.C) v = *reinterpret_cast<const uint4*>(qrow + ks * 32);
       qf[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -1056,12 +1099,12 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
   float m = kNegInf, l = 0.0f;
 
   const int nblk = t.k1 > t.k0 ? (t.k1 - t.k0 + C::BN - 1) / C::BN : 0;
-  const int lim = p.P0 + row;  // last visible key of this lane's row
+  const int lim = t.P0 + row;  // last visible key of this lane's row
 
   int* pids = lb.pids;
   const int pg0 = t.k0 / kPageSize;
-  const int pg1 = min((p.Lp + kPageSize - 1) / kPageSize, (t.k0 + nblk * C::BN + kPageSize - 1) / kPageSize);
-  preload_page_ids(p, pg0, pg1 - pg0, pids);
+  const int pg1 = min((t.Lp + kPageSize - 1) / kPageSize, (t.k0 + nblk * C::BN + kPageSize - 1) / kPageSize);
+  preload_page_ids(t.pt, p.num_pages, pg0, pg1 - pg0, pids);
   __syncthreads();
 
   if (nblk > 0) {
@@ -1071,10 +1114,10 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
       prefill_issue_block<D>(kpool, vpool, tok_bytes,
-                             __builtin_amdgcn_readfirstlane(pids[prefill_wave_page_index<D>(kb_of(s), p.Lp, pg0)]),
-                             p.Lp, kb_of(s), dma, lb.st[s]);
+                             __builtin_amdgcn_readfirstlane(pids[prefill_wave_page_index<D>(kb_of(s), t.Lp, pg0)]),
+                             t.Lp, kb_of(s), dma, lb.st[s]);
     // page id of the next block to issue, read one step ahead of its use
-    int pid_next = pids[prefill_wave_page_index<D>(kb_of(C::NS - 1), p.Lp, pg0)];
+    int pid_next = pids[prefill_wave_page_index<D>(kb_of(C::NS - 1), t.Lp, pg0)];
     // per-lane LDS byte offsets of the MFMA operands inside a stage
     const int krow_off = rl * C::ROWB;
     const int ksw = ksw_rows<C::CH>(rl);
@@ -1099,7 +1142,7 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
     // holds the rare branches: the causal mask of a diagonal block and the
     // rescale of o and l; it returns -max.
     auto softmax_max = [&](f32x16_t& sc, int kb0) __attribute__((always_inline)) {
-      if ((kb0 + C::BN - 1) > (p.P0 + t.row0)) {  // diagonal block: causal mask
+      if ((kb0 + C::BN - 1) > (t.P0 + t.row0)) {  // diagonal block: causal mask
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = kb0 + 8 * (j >> 2) + 4 * half + (j & 3);
@@ -1178,9 +1221,9 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
         wait_vm_lgkm<C::LPB * (C::NS - 3)>();
         __builtin_amdgcn_s_barrier();
         const int page = __builtin_amdgcn_readfirstlane(pid_next);
-        prefill_issue_block<D>(kpool, vpool, tok_bytes, page, p.Lp, kb_of(b + C::NS - 1), dma,
+        prefill_issue_block<D>(kpool, vpool, tok_bytes, page, t.Lp, kb_of(b + C::NS - 1), dma,
                                lb.st[(u + C::NS - 1) % C::NS]);
-        pid_next = pids[prefill_wave_page_index<D>(kb_of(b + C::NS), p.Lp, pg0)];
+        pid_next = pids[prefill_wave_page_index<D>(kb_of(b + C::NS), t.Lp, pg0)];
         // Blocks past the wave's causal end are fully masked (weights 0), and
         // the QK past the last block reads a stage that holds the last block
         // again and is never used, so the body needs no further branches.
@@ -1201,10 +1244,10 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
   __syncthreads();
 
   const float ltot = l + xor_lane(l, 32);
-  if (p.splits == 1) {
-    if (row < p.C) {
+  if (t.splits == 1) {
+    if (row < t.C) {
       const float inv = 1.0f / ltot;
-      char* orow = reinterpret_cast<char*>(p.op) + ((int64_t)row * p.hq + t.head) * D * 2;
+      char* orow = reinterpret_cast<char*>(p.op) + ((int64_t)(t.row_base + row) * p.hq + t.head) * D * 2;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1255,11 +1298,11 @@ DEV void prefill_tile_f32(const PodParams& p, int task, const LdsBufs& lb) {
 
   float q[D], acc[D];
   {
-    const float* qrow = reinterpret_cast<const float*>(p.qp) + ((int64_t)row * p.hq + t.head) * D;
+    const float* qrow = reinterpret_cast<const float*>(p.qp) + ((int64_t)(t.row_base + row) * p.hq + t.head) * D;
 #pragma unroll
     for (int e = 0; e < D; e += 4) {
       float4 v = make_float4(0, 0, 0, 0);
-      if (row < p.C) v = *reinterpret_cast<const float4*>(qrow + e);
+      if (row < t.C) v = *reinterpret_cast<const float4*>(qrow + e);
       q[e] = v.x;
       q[e + 1] = v.y;
       q[e + 2] = v.z;
@@ -1269,7 +1312,7 @@ DEV void prefill_tile_f32(const PodParams& p, int task, const LdsBufs& lb) {
 #pragma unroll
   for (int e = 0; e < D; ++e) acc[e] = 0.0f;
   float m = kNegInf, l = 0.0f;
-  const int lim = p.P0 + row;
+  const int lim = t.P0 + row;
   const int nblk = t.k1 > t.k0 ? (t.k1 - t.k0 + C::BN - 1) / C::BN : 0;
   const int64_t tok = (int64_t)p.hkv * D;
   const float* kpool = reinterpret_cast<const float*>(p.k_pool) + (int64_t)t.g * D;
@@ -1282,8 +1325,8 @@ DEV void prefill_tile_f32(const PodParams& p, int task, const LdsBufs& lb) {
       const int kk = idx / (D / 4), c = idx % (D / 4);
       const int key = kb0 + kk;
       float4 kv = make_float4(0, 0, 0, 0), vv = kv;
-      if (key < p.Lp) {
-        const int64_t page = min((uint32_t)p.pt_p[key >> 4], p.num_pages - 1u);
+      if (key < t.Lp) {
+        const int64_t page = min((uint32_t)t.pt[key >> 4], p.num_pages - 1u);
         const int64_t off = (page * kPageSize + (key & 15)) * tok + 4 * c;
         kv = *reinterpret_cast<const float4*>(kpool + off);
         vv = *reinterpret_cast<const float4*>(vpool + off);
@@ -1324,10 +1367,10 @@ DEV void prefill_tile_f32(const PodParams& p, int task, const LdsBufs& lb) {
       acc[e] = a;
     }
   }
-  if (p.splits == 1) {
-    if (row < p.C) {
+  if (t.splits == 1) {
+    if (row < t.C) {
       const float inv = 1.0f / l;
-      float* orow = reinterpret_cast<float*>(p.op) + ((int64_t)row * p.hq + t.head) * D;
+      float* orow = reinterpret_cast<float*>(p.op) + ((int64_t)(t.row_base + row) * p.hq + t.head) * D;
 #pragma unroll
       for (int e = 0; e < D; e += 4)
         *reinterpret_cast<float4*>(orow + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);

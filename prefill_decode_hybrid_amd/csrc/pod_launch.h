@@ -10,6 +10,16 @@
 
 namespace pod {
 
+// One prefill chunk as the kernels see it.  Its tasks are
+// task_base .. task_base + tiles * splits - 1 (tiles = row_blocks * hkv *
+// head_groups), its tiles tile_base .., its query/output rows row_base ..
+// row_base + C - 1 of the packed q and o, and its page ids start at entry
+// pt_base of the prefill page table.
+struct PfChunk {
+  int task_base, tile_base, row_base, pt_base;
+  int C, P0, splits, split_keys, row_blocks;
+};
+
 struct PodParams {
   // paged KV pool [num_pages, 16, hkv, d]
   const void* k_pool;
@@ -18,12 +28,12 @@ struct PodParams {
   int hq, hkv;
   float scale_log2;  // softmax scale * log2(e): scores live in the base-2 domain
 
-  // prefill chunk
+  // prefill chunks, in task order
   const void* qp;
   void* op;
   const int32_t* pt_p;
-  int C, P0, Lp;
-  int rows_per_tile, heads_per_tile, row_blocks, head_groups, tiles, splits, split_keys, p_tasks;
+  int rows_per_tile, heads_per_tile, head_groups, p_tasks, n_chunks;
+  PfChunk ch[kMaxChunks];  // read with a uniform index from the kernel-argument segment
   float* p_part;     // [task]: acc [row-head][d], m [row-head], l [row-head]
   uint32_t* p_cnt;   // [tile] arrival counters, 0 between calls
 

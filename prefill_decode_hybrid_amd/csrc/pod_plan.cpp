@@ -40,9 +40,13 @@ void derive_capacities(const Shape& s, Limits& lim) {
   int rpw, hpt, rw, rpt, hg;
   tile_geometry(s, rpw, hpt, rw, rpt, hg);
   const int64_t slots = (int64_t)lim.num_cus * lim.wg_per_cu;
-  lim.cap_tiles = ceil_div(std::max(1, lim.max_chunk_len), rpt) * s.hkv * hg;
+  // max_chunk_len bounds the rows of all chunks of a call; each chunk but
+  // the first may add one partial row block
+  const int64_t rows = std::max(1, lim.max_chunk_len);
+  lim.cap_tiles = (ceil_div(rows, rpt) + std::min<int64_t>(kMaxChunks, rows) - 1) * s.hkv * hg;
   lim.cap_prefill_tasks = std::max<int64_t>(
-      {1, lim.cap_waves * slots, lim.cap_tiles * ceil_div(std::max(1, lim.max_context), kMaxSplitKeys)});
+      {1, lim.cap_waves * slots + lim.cap_tiles,
+       lim.cap_tiles * ceil_div(std::max(1, lim.max_context), kMaxSplitKeys)});
   int64_t total = lim.max_total_context > 0 ? lim.max_total_context
                                             : (int64_t)lim.max_num_decode * lim.max_context;
   lim.cap_wave_tasks = (int64_t)s.hkv * (lim.max_num_decode + ceil_div(total, kMinSplitTokens));
@@ -104,30 +108,79 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   const int64_t slots = (int64_t)lim.num_cus * lim.wg_per_cu;
 
   if (pl.has_p) {
-    if (p.C < 1 || p.P0 < 0) return POD_ERR_INVALID_ARG;
-    if (p.C > lim.max_chunk_len || (int64_t)p.C + p.P0 > lim.max_context) return POD_ERR_INVALID_ARG;
-    pl.C = p.C;
-    pl.P0 = p.P0;
-    pl.Lp = p.C + p.P0;
+    if (p.n < 1 || p.n > kMaxChunks || p.stride < 0) return POD_ERR_INVALID_ARG;
+    int64_t rows = 0;
+    int row_base[kMaxChunks], order[kMaxChunks];
+    for (int c = 0; c < p.n; ++c) {
+      const int64_t Lp = (int64_t)p.C[c] + p.P0[c];
+      if (p.C[c] < 1 || p.P0[c] < 0 || Lp > lim.max_context) return POD_ERR_INVALID_ARG;
+      if (p.stride > 0 && ceil_div(Lp, kPageSize) > p.stride) return POD_ERR_INVALID_ARG;
+      row_base[c] = (int)rows;
+      rows += p.C[c];
+      order[c] = c;
+    }
+    if (rows > lim.max_chunk_len) return POD_ERR_INVALID_ARG;
     tile_geometry(s, pl.rows_per_wave, pl.heads_per_tile, pl.row_waves, pl.rows_per_tile,
                   pl.head_groups);
-    pl.row_blocks = (int)ceil_div(pl.C, pl.rows_per_tile);
-    pl.tiles = pl.row_blocks * s.hkv * pl.head_groups;
-    if (pl.tiles > lim.cap_tiles) return POD_ERR_WORKSPACE;
-    const int bn = keys_per_block(s.dtype);
-    int64_t splits = 1;
-    if (pl.tiles < slots) {
-      splits = ceil_div(slots, pl.tiles);
-      splits = std::min<int64_t>(splits, lim.cap_prefill_tasks / pl.tiles);
-      splits = std::min<int64_t>(splits, ceil_div(pl.Lp, kMinPrefillSplitKeys));
-      splits = std::max<int64_t>(splits, 1);
+    // Tasks run chunk by chunk, the longest key range first (its tiles take
+    // longest), the caller's order among equals.
+    std::stable_sort(order, order + p.n,
+                     [&](int a, int b) { return p.C[a] + p.P0[a] > p.C[b] + p.P0[b]; });
+    pl.n_chunks = p.n;
+    pl.stride = p.stride;
+    int64_t tiles = 0;
+    double work = 0.0;  // tiles x keys
+    for (int k = 0; k < p.n; ++k) {
+      ChunkPlan& ch = pl.ch[k];
+      ch.src = order[k];
+      ch.C = p.C[ch.src];
+      ch.P0 = p.P0[ch.src];
+      ch.Lp = ch.C + ch.P0;
+      ch.row_base = row_base[ch.src];
+      ch.row_blocks = (int)ceil_div(ch.C, pl.rows_per_tile);
+      ch.tiles = ch.row_blocks * s.hkv * pl.head_groups;
+      ch.tile_base = (int)tiles;
+      tiles += ch.tiles;
+      work += (double)ch.tiles * ch.Lp;
     }
-    splits = std::max<int64_t>(splits, ceil_div(pl.Lp, kMaxSplitKeys));
-    pl.split_keys = (int)round_up(ceil_div(pl.Lp, splits), bn);
-    pl.splits = (int)ceil_div(pl.Lp, pl.split_keys);  // drop splits left empty by rounding
-    pl.p_tasks = pl.tiles * pl.splits;
-    if (pl.splits > 1 && pl.p_tasks > lim.cap_prefill_tasks) return POD_ERR_WORKSPACE;
-    if (pl.split_keys > kMaxSplitKeys) return POD_ERR_WORKSPACE;
+    if (tiles > lim.cap_tiles) return POD_ERR_WORKSPACE;
+    pl.tiles = (int)tiles;
+    const int bn = keys_per_block(s.dtype);
+    // KV splits.  When the tiles do not fill the machine, the average tile
+    // is split s_par ways (at most cap_waves waves of workgroups in all) and
+    // each chunk in proportion to its key range, so tasks carry similar
+    // numbers of keys; a split added for parallelism keeps at least
+    // kMinPrefillSplitKeys keys, and no split exceeds kMaxSplitKeys (its page
+    // ids are staged in LDS).
+    auto assign = [&](int64_t s_par) {
+      int64_t tasks = 0;
+      for (int k = 0; k < p.n; ++k) {
+        ChunkPlan& ch = pl.ch[k];
+        int64_t sp = 1;
+        if (s_par > 1) {
+          sp = (int64_t)std::floor((double)s_par * (double)tiles * ch.Lp / work);
+          sp = std::max<int64_t>(1, std::min<int64_t>(sp, ceil_div(ch.Lp, kMinPrefillSplitKeys)));
+        }
+        sp = std::max<int64_t>(sp, ceil_div(ch.Lp, kMaxSplitKeys));
+        ch.split_keys = (int)round_up(ceil_div(ch.Lp, sp), bn);
+        ch.splits = (int)ceil_div(ch.Lp, ch.split_keys);  // drop splits left empty by rounding
+        ch.task_base = (int)tasks;
+        tasks += (int64_t)ch.tiles * ch.splits;
+      }
+      return tasks;
+    };
+    int64_t s_par = 1;
+    if (tiles < slots)
+      s_par = std::max<int64_t>(1, std::min<int64_t>(ceil_div(slots, tiles), lim.cap_waves * slots / tiles));
+    int64_t tasks = assign(s_par);
+    if (tasks > lim.cap_prefill_tasks) tasks = assign(1);
+    bool split = false;
+    for (int k = 0; k < p.n; ++k) {
+      split |= pl.ch[k].splits > 1;
+      if (pl.ch[k].split_keys > kMaxSplitKeys) return POD_ERR_WORKSPACE;
+    }
+    if (tasks > (1LL << 30) || (split && tasks > lim.cap_prefill_tasks)) return POD_ERR_WORKSPACE;
+    pl.p_tasks = (int)tasks;
   }
 
   if (pl.has_d) {
@@ -169,8 +222,12 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   //    so every tile starts at once beside the decodes.
   if (pl.has_p && pl.has_d) {
     const double es = s.dtype == kBf16 ? 2.0 : 4.0;
-    const double f_p = 4.0 * s.d * s.hq * ((double)pl.C * pl.P0 + 0.5 * pl.C * (pl.C + 1.0));
-    const double t_task = (double)std::min(pl.Lp, pl.split_keys) * kPrefillSecondsPerKey;
+    double f_p = 0.0, t_task = 0.0;
+    for (int k = 0; k < pl.n_chunks; ++k) {
+      const ChunkPlan& ch = pl.ch[k];
+      f_p += 4.0 * s.d * s.hq * ((double)ch.C * ch.P0 + 0.5 * ch.C * (ch.C + 1.0));
+      t_task = std::max(t_task, (double)std::min(ch.Lp, ch.split_keys) * kPrefillSecondsPerKey);
+    }
     const double t_p = std::max(t_task, f_p / (s.dtype == kBf16 ? kPrefillFlopsBf16 : kPrefillFlopsF32));
     const double t_d = 2.0 * s.hkv * s.d * es * (double)pl.d_total / kDecodeBytesPerS;
     if (lim.slots_x256 > 0)

@@ -2,8 +2,8 @@
 // so it is unit-testable on a machine without a GPU.
 //
 // A plan turns one call's shapes into the task lists the kernels walk:
-//  * prefill tiles (row block, kv head, head group), each split into KV
-//    ranges when there are too few tiles to fill the machine.  The number of
+//  * prefill tiles (chunk, row block, kv head, head group), each split into
+//    KV ranges when there are too few tiles to fill the machine.  The number of
 //    prefill tasks is capped at `cap_waves` waves of resident workgroups so a
 //    chunk cannot flood the launch (paper §4.2.3 caps chunked-prefill splits
 //    at two full waves);
@@ -30,6 +30,7 @@ constexpr int kMaxContext = 1023 * kMinSplitTokens;  // 261888 tokens: <= 1023 d
 constexpr int kMinPrefillSplitKeys = 1024;
 constexpr int kMaxSplitKeys = 16384;       // page ids of one split are staged in LDS
 constexpr int kShareDen = 64;
+constexpr int kMaxChunks = 16;             // prefill chunks of one call
 // Throughput of the split kernels on MI355X, used only to pick the fused
 // launch's per-CU prefill slots: prefill FLOP/s (bf16 and fp32 tiles) and
 // decode bytes/s over the whole chip, and the decode time below which a
@@ -56,9 +57,21 @@ struct Limits {
   int64_t cap_prefill_tasks = 0, cap_wave_tasks = 0, cap_tiles = 0;
 };
 
+// Prefill chunks of one call in the caller's order.  stride: page-table
+// row stride of chunk c (row c of the table); 0 for the single-chunk call,
+// whose table is one row.
 struct PrefillIn {
   bool present = false;
-  int C = 0, P0 = 0;
+  int n = 0, stride = 0;
+  int C[kMaxChunks] = {}, P0[kMaxChunks] = {};
+};
+
+// One chunk of a plan.  Chunks are laid out in task order (longest key
+// range first); src is the caller's index of the chunk.
+struct ChunkPlan {
+  int src = 0, C = 0, P0 = 0, Lp = 0;
+  int row_blocks = 0, tiles = 0, splits = 0, split_keys = 0;
+  int task_base = 0, tile_base = 0, row_base = 0;
 };
 
 struct DecodeIn {
@@ -71,9 +84,10 @@ struct Plan {
   int mode = 0, fallback = 0, num_cus = 0, wg_per_cu = 0, grid = 0;
   // prefill
   bool has_p = false;
-  int C = 0, P0 = 0, Lp = 0;
-  int rows_per_wave = 0, heads_per_tile = 0, row_waves = 0, rows_per_tile = 0;
-  int row_blocks = 0, head_groups = 0, tiles = 0, splits = 0, split_keys = 0, p_tasks = 0;
+  int n_chunks = 0, stride = 0;
+  ChunkPlan ch[kMaxChunks];
+  int rows_per_wave = 0, heads_per_tile = 0, row_waves = 0, rows_per_tile = 0, head_groups = 0;
+  int tiles = 0, p_tasks = 0;  // over all chunks
   // decode
   bool has_d = false;
   int N = 0, T = 0, d_wave_tasks = 0, d_wg_tasks = 0;

@@ -1,5 +1,5 @@
-"""Seeded synthetic hybrid batches: one chunked-prefill request plus N decodes
-over a paged GQA KV cache.
+"""Seeded synthetic hybrid batches: one chunked-prefill request (or several,
+with a "chunks" list) plus N decodes over a paged GQA KV cache.
 
 This module only draws numbers and lays them out; it holds none of the
 attention arithmetic. Both the HIP path and the fp64 oracle consume what it
@@ -17,7 +17,7 @@ Readings where the pages are silent (each is listed in the design doc):
   * Softmax scale = 1/sqrt(d).
   * A request's own K/V (including the prefill chunk's and each decode's
     current token) are already in the pool.
-  * Pool pages are handed out prefill-request first, then decodes in order;
+  * Pool pages are handed out prefill request(s) first, then decodes in order;
     physical ids are a seeded permutation (identity for "contiguous KV").
   * Slots past a request's length in its last page are NaN, page-table
     padding points at one extra all-NaN guard page, so a kernel that reads
@@ -65,11 +65,12 @@ _GEN_CHUNK_PAGES = 2048  # fixed so the draw order never depends on memory
 class HybridBatch:
     """One hybrid batch, all tensors on the CPU.
 
-    q_prefill   [C, Hq, d]            dtype
+    q_prefill   [C, Hq, d]            dtype (several chunks: their rows back to back)
     q_decode    [N, Hq, d]            dtype
     k_pool      [num_pages+1, B, Hkv, d]  (last page = NaN guard)
     v_pool      same as k_pool
-    page_table_prefill [ceil((P0+C)/B)] int32
+    page_table_prefill [ceil((P0+C)/B)] int32 (several chunks: [n, stride],
+                                        padding -> guard page)
     page_table_decode  [N, stride]      int32 (padding -> guard page)
     context_lens       [N]              int32
     """
@@ -87,6 +88,7 @@ class HybridBatch:
     sm_scale: float
     guard_page: int
     outlier_rows: int = 0
+    chunks: Optional[list] = None  # several chunks: [(chunk_len, chunk_offset), ...]
 
     @property
     def num_q_heads(self): return self.spec["num_q_heads"]
@@ -110,12 +112,17 @@ class HybridBatch:
             context_lens=mv(self.context_lens))
 
     # ---- work counts (used for reporting; nothing here is attention math) ----
+    def chunk_list(self) -> list:
+        """[(chunk_len, chunk_offset)] of every prefill chunk ([] without prefill)."""
+        if self.q_prefill is None:
+            return []
+        return list(self.chunks) if self.chunks is not None else [(self.chunk_len, self.chunk_offset)]
+
     def visible_keys_prefill(self) -> int:
-        c, p0 = self.chunk_len, self.chunk_offset
-        return 0 if self.q_prefill is None else c * p0 + c * (c + 1) // 2
+        return sum(c * p0 + c * (c + 1) // 2 for c, p0 in self.chunk_list())
 
     def kv_tokens(self) -> int:
-        lp = 0 if self.q_prefill is None else self.chunk_offset + self.chunk_len
+        lp = sum(c + p0 for c, p0 in self.chunk_list())
         ld = 0 if self.context_lens is None else int(self.context_lens.sum())
         return lp + ld
 
@@ -170,13 +177,19 @@ def make_batch(spec, seed: int = 0, with_prefill: bool = True, with_decode: bool
     ss = np.random.SeedSequence(seed).spawn(len(_STREAMS))
     rngs = {name: np.random.Generator(np.random.PCG64(s)) for name, s in zip(_STREAMS, ss)}
 
-    C, P0 = int(spec["chunk_len"]), int(spec["chunk_offset"])
-    Lp = P0 + C
+    multi = spec.get("chunks") is not None
+    if multi:
+        chunks = [(int(c), int(p)) for c, p in spec["chunks"]]
+        C, P0 = sum(c for c, _ in chunks), 0
+    else:
+        C, P0 = int(spec["chunk_len"]), int(spec["chunk_offset"])
+        chunks = [(C, P0)]
     lens = _draw_lengths(spec["decode_lens"], rngs["lengths"]) if with_decode else np.zeros(0, np.int64)
     N = len(lens)
+    n_pre = len(chunks) if with_prefill else 0
 
-    # logical page lists: prefill request first, then decodes in order
-    req_lens = ([Lp] if with_prefill else []) + [int(x) for x in lens]
+    # logical page lists: prefill request(s) first, then decodes in order
+    req_lens = ([c + p for c, p in chunks] if with_prefill else []) + [int(x) for x in lens]
     req_pages = [-(-L // B) for L in req_lens]
     num_pages = int(sum(req_pages))
     if spec.get("contiguous", False):
@@ -222,12 +235,18 @@ def make_batch(spec, seed: int = 0, with_prefill: bool = True, with_decode: bool
     pt_p = None
     q_p = None
     if with_prefill:
-        pt_p = torch.from_numpy(req_phys[0].astype(np.int32))
+        if multi:
+            pt = np.full((n_pre, max(req_pages[:n_pre])), guard, dtype=np.int32)
+            for i in range(n_pre):
+                pt[i, :len(req_phys[i])] = req_phys[i]
+            pt_p = torch.from_numpy(pt)
+        else:
+            pt_p = torch.from_numpy(req_phys[0].astype(np.int32))
         q_p = torch.from_numpy(_normal(rngs["q_prefill"], (C, hq, d), scale)).to(dtype)
 
     pt_d = q_d = ctx = None
     if with_decode and N > 0:
-        first = 1 if with_prefill else 0
+        first = n_pre
         stride = max(req_pages[first:])
         pt = np.full((N, stride), guard, dtype=np.int32)
         for i in range(N):
@@ -242,7 +261,8 @@ def make_batch(spec, seed: int = 0, with_prefill: bool = True, with_decode: bool
                        page_table_decode=pt_d, context_lens=ctx,
                        chunk_len=C if with_prefill else 0,
                        chunk_offset=P0 if with_prefill else 0,
-                       sm_scale=float(sm_scale), guard_page=guard, outlier_rows=n_out)
+                       sm_scale=float(sm_scale), guard_page=guard, outlier_rows=n_out,
+                       chunks=chunks if (multi and with_prefill) else None)
 
 
 def draw_context_lens(spec, seed: int = 0) -> np.ndarray:
