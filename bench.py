@@ -44,11 +44,11 @@ def work_counts(b):
     hq, hkv, d = b.num_q_heads, b.num_kv_heads, b.head_dim
     s = 2 if b.spec["dtype"] == "bf16" else 4
     lens = [] if b.context_lens is None else [int(x) for x in b.context_lens]
-    C, P0 = b.chunk_len, b.chunk_offset
-    f_prefill = 4.0 * d * hq * (C * P0 + C * (C + 1) / 2)
+    rows = sum(c for c, _ in b.chunk_list())
+    f_prefill = 4.0 * d * hq * b.visible_keys_prefill()  # causal: row i sees P0 + i + 1 keys
     f_decode = 4.0 * d * hq * sum(lens)
-    bytes_kv = 2.0 * hkv * d * s * ((C + P0) + sum(lens))
-    bytes_qo = 2.0 * (C + len(lens)) * hq * d * s
+    bytes_kv = 2.0 * hkv * d * s * b.kv_tokens()  # every visible K and V row once
+    bytes_qo = 2.0 * (rows + len(lens)) * hq * d * s
     return dict(f_prefill=f_prefill, f_decode=f_decode, bytes_kv=bytes_kv, bytes_qo=bytes_qo,
                 bytes_total=bytes_kv + bytes_qo)
 

@@ -22,7 +22,6 @@ from __future__ import annotations
 import argparse
 import dataclasses
 import json
-import statistics
 import sys
 import time
 
@@ -54,6 +53,7 @@ def main(argv=None):
     import torch
     import prefill_decode_hybrid_amd as pod
     from prefill_decode_hybrid_amd import inputs
+    from prefill_decode_hybrid_amd.timing import interleaved_us, on_two_streams
 
     if not torch.cuda.is_available():
         sys.exit("the sweep needs a GPU")
@@ -90,18 +90,8 @@ def main(argv=None):
             att.decode_only(b, od2, ctx_host)
 
         def streams():
-            main_s = torch.cuda.current_stream()
-            fork = torch.cuda.Event()
-            fork.record(main_s)
-            s1.wait_event(fork)
-            s2.wait_event(fork)
-            att.prefill_only(b, op2, stream=s1)
-            att.decode_only(b, od2, ctx_host, stream=s2)
-            j1, j2 = torch.cuda.Event(), torch.cuda.Event()
-            j1.record(s1)
-            j2.record(s2)
-            main_s.wait_event(j1)
-            main_s.wait_event(j2)
+            on_two_streams(lambda s: att.prefill_only(b, op2, stream=s),
+                           lambda s: att.decode_only(b, od2, ctx_host, stream=s), s1, s2)
 
         fused()
         plan = att.stats()
@@ -109,21 +99,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         same = bool(torch.equal(op, op2) and torch.equal(od, od2))
         all_same &= same
-        for _ in range(a.warmup):
-            fused()
-            serial()
-            streams()
-        ts = [[], [], []]
-        for _ in range(a.steps):
-            for k, fn in enumerate((fused, serial, streams)):
-                flush.zero_()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                ts[k].append((e0, e1))
-        torch.cuda.synchronize()
-        med = [statistics.median(x.elapsed_time(y) for x, y in t) * 1e3 for t in ts]
+        med = interleaved_us((fused, serial, streams), a.steps, a.warmup, flush)
         rows.append({"chunk": i, "offset": p0, "fused_us": round(med[0], 1), "serial_us": round(med[1], 1),
                      "two_stream_us": round(med[2], 1), "prefill_tasks": plan["prefill_tasks"],
                      "prefill_splits": plan["prefill_splits"], "cu_prefill_x256": plan["cu_prefill_x256"],

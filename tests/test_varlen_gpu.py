@@ -7,6 +7,9 @@ one chunk (bf16: max |err| <= 2e-2, mean <= 2e-3; fp32: max <= 1e-4).  The
 fused call must equal the split calls bit for bit, and a one-chunk varlen
 call must equal the single-chunk entry point bit for bit."""
 import dataclasses
+import io
+import json
+from contextlib import redirect_stdout
 
 import numpy as np
 import pytest
@@ -14,7 +17,7 @@ import torch
 
 import oracle
 import prefill_decode_hybrid_amd as pod
-from prefill_decode_hybrid_amd import inputs
+from prefill_decode_hybrid_amd import inputs, multichunk
 from gpu_helpers import TOL, errors, sample_reqs, sample_rows, say
 
 pytestmark = pytest.mark.gpu
@@ -156,3 +159,13 @@ def test_four_prompts_beside_long_decodes():
         check(b, op, od, "four prompts", rows_per_chunk=rows, reqs=sample_reqs(b.context_lens.tolist()))
     finally:
         att.close()
+
+
+def test_multichunk_cli_small():
+    buf = io.StringIO()
+    with redirect_stdout(buf):
+        multichunk.main(["--chunks", "100@0,64@900,7@3", "--num-decode", "4", "--decode-context", "2048",
+                         "--steps", "2", "--warmup", "1"])
+    out = json.loads(buf.getvalue().strip().splitlines()[-1])
+    assert out["fused_equals_split"] and out["plan"]["prefill_chunks"] == 3
+    assert out["fused_us"] > 0 and out["serial_us"] > 0 and out["two_stream_us"] > 0
