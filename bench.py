@@ -166,6 +166,8 @@ def main():
     ap.add_argument("--counters-driver", action="store_true",
                     help="run each entry point untimed (the workload for rocprofv3 --pmc passes) and exit")
     ap.add_argument("--policy", type=int, default=0, help="fused role policy (enum pod_policy)")
+    ap.add_argument("--persistent", action="store_true",
+                    help="fused launch as a resident grid looping over the task queues")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this hot path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -187,7 +189,7 @@ def main():
     log(f"[bench] generated in {time.time() - t0:.1f}s: {inputs.describe(batch)}")
     dev = batch.to("cuda:0")
     ctx_host = batch.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(batch, policy=args.policy))
+    att = pod.PodAttention(pod.config_for_batch(batch, policy=args.policy, persistent=int(args.persistent)))
     op = torch.empty_like(dev.q_prefill)
     od = torch.empty_like(dev.q_decode)
     op2 = torch.empty_like(dev.q_prefill)

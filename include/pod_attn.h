@@ -110,6 +110,10 @@ typedef struct {
                                  256 .. 4096; 0 selects the planner's choice, which
                                  depends on the decode batch alone (so a decode's result
                                  has the same bits in fused and decode-only launches)  */
+    int32_t persistent;         /* 1: the fused launch is a resident grid (CUs x
+                                 wg_per_cu workgroups) that loops over the task queues
+                                 until both are empty, instead of one workgroup per
+                                 task; same tasks and results.  0: one per task       */
 } pod_attn_config;
 
 typedef struct {
@@ -173,6 +177,7 @@ typedef struct {
                                    averaged over CUs, in 1/256                        */
     int32_t policy;
     int32_t prefill_chunks;     /* prefill chunks of the call (0 without prefill)     */
+    int32_t persistent;         /* 1 if the fused launch ran as a resident grid       */
 } pod_attn_stats;
 
 /* Validate `cfg`, pick the device, reserve the workspace.  Returns POD_OK and

@@ -39,7 +39,8 @@ class PodAttnConfig(ctypes.Structure):
                 ("max_context", ctypes.c_int32), ("max_total_context", ctypes.c_int64),
                 ("wg_per_cu", ctypes.c_int32), ("prefill_split_cap_waves", ctypes.c_int32),
                 ("policy", ctypes.c_int32), ("device", ctypes.c_int32),
-                ("prefill_slots_x256", ctypes.c_int32), ("decode_split_tokens", ctypes.c_int32)]
+                ("prefill_slots_x256", ctypes.c_int32), ("decode_split_tokens", ctypes.c_int32),
+                ("persistent", ctypes.c_int32)]
 
 
 class PodPrefillArgs(ctypes.Structure):
@@ -64,7 +65,7 @@ class PodAttnStats(ctypes.Structure):
         "mode", "fallback", "num_cus", "wg_per_cu", "grid", "prefill_rows_per_tile",
         "prefill_heads_per_tile", "prefill_tiles", "prefill_splits", "prefill_split_keys",
         "prefill_tasks", "decode_split_tokens", "decode_wave_tasks", "decode_wg_tasks",
-        "share_num", "share_den", "cu_prefill_x256", "policy", "prefill_chunks")]
+        "share_num", "share_den", "cu_prefill_x256", "policy", "prefill_chunks", "persistent")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -125,11 +126,11 @@ def make_config(dtype=POD_BF16, num_q_heads=32, num_kv_heads=8, head_dim=128, pa
                 sm_scale=0.0, max_chunk_len=4096, max_num_decode=256, max_context=32768,
                 max_total_context=0, wg_per_cu=0, prefill_split_cap_waves=0,
                 policy=POD_POLICY_CU_BALANCED, device=-1, prefill_slots_x256=0,
-                decode_split_tokens=0) -> PodAttnConfig:
+                decode_split_tokens=0, persistent=0) -> PodAttnConfig:
     return PodAttnConfig(dtype, num_q_heads, num_kv_heads, head_dim, page_size, sm_scale,
                          max_chunk_len, max_num_decode, max_context, max_total_context,
                          wg_per_cu, prefill_split_cap_waves, policy, device, prefill_slots_x256,
-                         decode_split_tokens)
+                         decode_split_tokens, persistent)
 
 
 def _ptr(t) -> Optional[int]:

@@ -48,6 +48,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   if (c->prefill_split_cap_waves < 0) return POD_ERR_INVALID_ARG;
   if (c->policy < pod::kPolicyCuBalanced || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
   if (c->prefill_slots_x256 < 0 || c->prefill_slots_x256 > 2 * 256) return POD_ERR_INVALID_ARG;
+  if (c->persistent != 0 && c->persistent != 1) return POD_ERR_INVALID_ARG;
   if (c->decode_split_tokens != 0 &&
       (c->decode_split_tokens % pod::kPageSize != 0 || c->decode_split_tokens < pod::kMinSplitTokens ||
        c->decode_split_tokens > pod::kMaxSplitTokens))
@@ -61,6 +62,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   lim.policy = c->policy;
   lim.slots_x256 = c->prefill_slots_x256;
   lim.split_tokens = c->decode_split_tokens;
+  lim.persistent = c->persistent != 0;
   scale = c->sm_scale > 0.0f ? c->sm_scale : 1.0f / std::sqrt((float)s.d);
   return POD_OK;
 }
@@ -76,6 +78,7 @@ void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
   st->prefill_heads_per_tile = pl.heads_per_tile;
   st->prefill_tiles = pl.tiles;
   st->prefill_chunks = pl.has_p ? pl.n_chunks : 0;
+  st->persistent = pl.persistent ? 1 : 0;
   st->prefill_splits = pl.has_p ? pl.ch[0].splits : 0;
   st->prefill_split_keys = pl.has_p ? pl.ch[0].split_keys : 0;
   st->prefill_tasks = pl.has_p ? pl.p_tasks : 0;

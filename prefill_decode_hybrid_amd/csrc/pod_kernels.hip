@@ -754,14 +754,18 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
       m = mnew;
     }
     const float mu = safe_max(m);
+    // The row sum adds the same bf16 weights the PV product uses, so the
+    // normalised weights sum to one: a dominant weight's rounding cancels
+    // instead of scaling the whole output.
     uint32_t pw[4];
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       const float e0 = fast_exp2(sc[pp][0] - mu), e1 = fast_exp2(sc[pp][1] - mu);
       const float e2 = fast_exp2(sc[pp][2] - mu), e3 = fast_exp2(sc[pp][3] - mu);
-      l += (e0 + e1) + (e2 + e3);
       pw[2 * pp] = pack_bf16(e0, e1);
       pw[2 * pp + 1] = pack_bf16(e2, e3);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[2 * pp]), kOnes2, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[2 * pp + 1]), kOnes2, l, false);
     }
     const bf16x8_t pf = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
     // O^T += V^T P^T; lane (quad q4, i = 4k + j) reads keys 4*q4 + k of each
@@ -1485,6 +1489,58 @@ DEV bool claim_decode(const PodParams& p, uint32_t xcc, int& task) {
   return t < (uint32_t)p.d_wg_tasks;
 }
 
+// Role choice and task claim of one workgroup (thread 0) under the policies
+// below.  Sets `task` past its role's count when both queues are empty.
+DEV void pick_and_claim(const PodParams& p, int& role, int& task, bool& counted, uint32_t& key) {
+  key = cu_key();
+  const uint32_t xcc = (key >> 8) & 7u;
+  uint32_t* word = p.tickets + key;
+  counted = p.policy == kPolicyCuBalanced;
+  if (p.policy == kPolicyCuBalanced) {
+    const uint32_t frac = ((key * 2654435761u) >> 24) & 255u;
+    const uint32_t target = ((uint32_t)p.cu_prefill_x256 >> 8) + (frac < ((uint32_t)p.cu_prefill_x256 & 255u) ? 1u : 0u);
+    uint32_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t pdone = ctrl_load(p.ctrl + kCtrlPrefillDone), ddone = ctrl_load(p.ctrl + kCtrlDecodeDone);
+    if (pdone | ddone) {
+      // one queue is empty: take the other, uncounted (the mix no longer matters)
+      role = pdone ? 1 : 0;
+      counted = false;
+    } else {
+      while (true) {
+        role = (old & 0xffffu) < target ? 0 : 1;
+        const uint32_t nw = old + (role == 0 ? 1u : 0x10000u);
+        if (__hip_atomic_compare_exchange_strong(word, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+          break;
+      }
+    }
+  } else if (p.policy == kPolicyStatic) {
+    // (persistent grid only) prefill until its queue is empty, then decode
+    role = ctrl_load(p.ctrl + kCtrlPrefillDone) ? 1 : 0;
+  } else {
+    const uint32_t t = atomicAdd(word, 1u) % (uint32_t)p.share_den;
+    const uint32_t num = (uint32_t)p.share_num, den = (uint32_t)p.share_den;
+    role = ((t + 1) * num + den - 1) / den > (t * num + den - 1) / den ? 0 : 1;
+  }
+  const int want = role;
+  bool ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, xcc, task);
+  if (!ok) {
+    role ^= 1;
+    ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, xcc, task);
+  }
+  if (!ok && counted) {  // nothing left: undo the count
+    atomicSub(word, want == 0 ? 1u : 0x10000u);
+    counted = false;
+  } else if (counted && role != want) {  // recount under the role actually taken
+    atomicAdd(word, role == 0 ? 1u - 0x10000u : 0x10000u - 1u);
+  }
+}
+
+DEV void clear_next_ctrl(const PodParams& p) {
+  for (int q = 0; q < kCtrlUsed; ++q)
+    __hip_atomic_store(p.ctrl_next + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Fused hybrid kernel.  A regular grid of prefill tasks + decode workgroup
 // tasks is launched; each workgroup picks its role after dispatch from the
 // compute unit it landed on (paper §4.1) and then claims a task of that role,
@@ -1508,52 +1564,18 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   __shared__ uint32_t cu_word;
   if (threadIdx.x == 0) {
     int role, task = 0;
-    bool counted = p.policy == kPolicyCuBalanced;
+    bool counted = false;
+    uint32_t key = 0;
     if (p.policy == kPolicyStatic) {
       role = (int)blockIdx.x < p.p_tasks ? 0 : 1;
       task = role == 0 ? (int)blockIdx.x : (int)blockIdx.x - p.p_tasks;
     } else {
-      const uint32_t key = cu_key();
-      const uint32_t xcc = (key >> 8) & 7u;
-      uint32_t* word = p.tickets + key;
-      if (p.policy == kPolicyCuBalanced) {
-        const uint32_t frac = ((key * 2654435761u) >> 24) & 255u;
-        const uint32_t target = ((uint32_t)p.cu_prefill_x256 >> 8) + (frac < ((uint32_t)p.cu_prefill_x256 & 255u) ? 1u : 0u);
-        uint32_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t pdone = ctrl_load(p.ctrl + kCtrlPrefillDone), ddone = ctrl_load(p.ctrl + kCtrlDecodeDone);
-        if (pdone | ddone) {
-          // one queue is empty: take the other, uncounted (the mix no longer matters)
-          role = pdone ? 1 : 0;
-          counted = false;
-        } else {
-          while (true) {
-            role = (old & 0xffffu) < target ? 0 : 1;
-            const uint32_t nw = old + (role == 0 ? 1u : 0x10000u);
-            if (__hip_atomic_compare_exchange_strong(word, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT))
-              break;
-          }
-        }
-      } else {
-        const uint32_t t = atomicAdd(word, 1u) % (uint32_t)p.share_den;
-        const uint32_t num = (uint32_t)p.share_num, den = (uint32_t)p.share_den;
-        role = ((t + 1) * num + den - 1) / den > (t * num + den - 1) / den ? 0 : 1;
-      }
-      const int want = role;
-      bool ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, xcc, task);
-      if (!ok) {
-        role ^= 1;
-        ok = role == 0 ? claim_prefill(p, xcc, task) : claim_decode(p, xcc, task);
-      }
-      if (counted && role != want)  // recount under the role actually taken
-        atomicAdd(word, role == 0 ? 1u - 0x10000u : 0x10000u - 1u);
-      cu_word = key;
+      pick_and_claim(p, role, task, counted, key);
     }
     // The previous launch on this handle used the other block and has
     // finished (stream order); clear it for the next launch.
-    if (blockIdx.x == 0)
-      for (int q = 0; q < kCtrlUsed; ++q)
-        __hip_atomic_store(p.ctrl_next + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0) clear_next_ctrl(p);
+    cu_word = key;
     role_task[0] = role;
     role_task[1] = task;
     role_task[2] = counted;
@@ -1571,13 +1593,51 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   }
 }
 
+// Persistent variant of the fused kernel: a grid of (CUs x resident
+// workgroups) that loops — pick a role by the policy, claim a task of it,
+// run it, uncount — until both queues are empty (paper §4.3 mentions such a
+// variant performing on par).  Same tasks, same merges, same results.
+template <class E, int D, int G>
+__global__ __launch_bounds__(256, 2) void pod_persistent_kernel(PodParams p) {
+  POD_DECLARE_LDS(E, D);
+  __shared__ int role_task[3];
+  __shared__ uint32_t cu_word;
+  if (blockIdx.x == 0 && threadIdx.x == 0) clear_next_ctrl(p);
+  while (true) {
+    if (threadIdx.x == 0) {
+      int role, task = 0;
+      bool counted;
+      uint32_t key;
+      pick_and_claim(p, role, task, counted, key);
+      cu_word = key;
+      role_task[0] = role;
+      role_task[1] = task;
+      role_task[2] = counted;
+    }
+    __syncthreads();
+    const int role = role_task[0], task = role_task[1];
+    if (role == 0) {
+      if (task >= p.p_tasks) break;  // both queues empty (uniform: read from LDS)
+      PfSel<E, D>::run(p, task, lb);
+    } else {
+      if (task >= p.d_wg_tasks) break;
+      decode_wg<E, D, G, fused_pf<E, G>()>(p, task, lb);
+    }
+    __syncthreads();  // the task's LDS and role_task are free again
+    if (threadIdx.x == 0 && role_task[2]) atomicSub(p.tickets + cu_word, role == 0 ? 1u : 0x10000u);
+  }
+}
+
 // ------------------------------------------------------------------- launch
 template <class E, int D, int G>
 static int launch_t(int which, const PodParams& p, const Plan& pl, hipStream_t s) {
   const dim3 block(256);
   switch (which) {
     case kKernelHybrid:
-      hipLaunchKernelGGL((pod_hybrid_kernel<E, D, G>), dim3(pl.grid), block, 0, s, p);
+      if (pl.persistent)
+        hipLaunchKernelGGL((pod_persistent_kernel<E, D, G>), dim3(pl.grid), block, 0, s, p);
+      else
+        hipLaunchKernelGGL((pod_hybrid_kernel<E, D, G>), dim3(pl.grid), block, 0, s, p);
       break;
     case kKernelPrefill:
       hipLaunchKernelGGL((pod_prefill_kernel<E, D, G>), dim3(pl.p_tasks), block, 0, s, p);

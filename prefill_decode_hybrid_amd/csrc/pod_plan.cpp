@@ -273,6 +273,10 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   }
 
   pl.grid = (pl.has_p ? pl.p_tasks : 0) + (pl.has_d ? pl.d_wg_tasks : 0);
+  if (pl.has_p && pl.has_d && lim.persistent) {
+    pl.persistent = true;  // every resident slot loops over the queues
+    pl.grid = (int)std::min<int64_t>(pl.grid, slots);
+  }
   if (pl.has_p && pl.has_d) {
     if (lim.policy == kPolicyHalf) {
       pl.share_num = 1;

@@ -52,6 +52,7 @@ struct Limits {
   int wg_per_cu = 2, cap_waves = 2, policy = kPolicyCuBalanced;
   int slots_x256 = 0;  // prefill slots per CU for the CU-balanced policy; 0: from the batch
   int split_tokens = 0;  // decode tokens per wave task; 0: from the batch
+  bool persistent = false;  // fused launch as a resident grid looping over the queues
   int num_cus = 0;
   // capacities derived by workspace_layout()
   int64_t cap_prefill_tasks = 0, cap_wave_tasks = 0, cap_tiles = 0;
@@ -95,6 +96,7 @@ struct Plan {
   int d_full = 0;       // decode units that are full T-token splits
   // fused scheduling
   int share_num = 0, share_den = 1, cu_prefill_x256 = 0, policy = 0;
+  bool persistent = false;  // the fused launch is a resident grid of workgroups
 };
 
 // Rows of one wave's query block and keys per staged KV block, per dtype.

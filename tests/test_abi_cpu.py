@@ -276,3 +276,23 @@ def test_role_rule_is_proportional_and_prefill_first():
     for num, den in [(1, 9), (7, 64), (1, 2), (63, 64)]:
         roles = [((t + 1) * num + den - 1) // den > (t * num + den - 1) // den for t in range(den)]
         assert sum(roles) == num and roles[0]
+
+
+def test_persistent_plan():
+    spec = inputs.CONFIGS[3]
+    lens = inputs.draw_context_lens(3, 0)
+    a = plan(_cfg(3), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]), _decode(lens))
+    b = plan(_cfg(3, persistent=1), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
+             _decode(lens))
+    assert a["persistent"] == 0 and b["persistent"] == 1
+    assert b["grid"] == min(a["grid"], 256 * b["wg_per_cu"])
+    assert {k: v for k, v in a.items() if k not in ("grid", "persistent")} == \
+        {k: v for k, v in b.items() if k not in ("grid", "persistent")}
+    # split launches and one-sided calls keep one workgroup per task
+    for mode, pa, da in ((pod.MODE_PREFILL, _prefill(100, 0), None), (pod.MODE_DECODE, None, _decode([5, 9])),
+                         (pod.MODE_HYBRID, None, _decode([5, 9]))):
+        st = plan(_cfg(3, persistent=1), mode, pa, da)
+        assert st["persistent"] == 0
+    with pytest.raises(pod.PodAttnError) as e:
+        plan(_cfg(3, persistent=2), pod.MODE_DECODE, None, _decode([5]))
+    assert e.value.status == pod.POD_ERR_INVALID_ARG

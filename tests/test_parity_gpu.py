@@ -5,10 +5,10 @@ pod_attn_decode_only) is compared element by element with the oracle on the
 same seeded inputs.  Bars: bf16 inputs with fp32 accumulation, max abs error
 <= 2e-2 and mean abs error <= 2e-3; fp32 inputs, max abs error <= 1e-4.
 Small cases span several tiles and ragged tails and are compared in full; the
-five workload configs are compared in full (1, 2) or on sampled rows and
-requests (3, 4, 5: first/last rows, every tile edge, random rows; the
-shortest and longest requests plus random ones) in the launch configuration
-the benchmark times.  Fusion must not change the result: the fused call is
+five workload configs are compared in full (1-4: every row and request) or
+on sampled rows and requests (5: first/last rows, every tile edge, random
+rows; the shortest and longest requests plus random ones) in the launch
+configuration the benchmark times.  Fusion must not change the result: the fused call is
 bitwise equal to the two split calls, and repeated calls are bitwise equal.
 """
 import numpy as np
@@ -124,7 +124,7 @@ def config_run(cid):
     return _CACHE[cid]
 
 
-@pytest.mark.parametrize("cid", [1, 2])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
 def test_config_full(cid):
     run = config_run(cid)
     op, od = run.hybrid()
@@ -135,7 +135,7 @@ def test_config_full(cid):
     assert torch.equal(op, sp_) and torch.equal(od, sd_)
 
 
-@pytest.mark.parametrize("cid", [3, 4, 5])
+@pytest.mark.parametrize("cid", [5])
 def test_config_sampled(cid):
     run = config_run(cid)
     op, od = run.hybrid()
