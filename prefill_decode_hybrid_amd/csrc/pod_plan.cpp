@@ -150,8 +150,9 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     // is split s_par ways (at most cap_waves waves of workgroups in all) and
     // each chunk in proportion to its key range, so tasks carry similar
     // numbers of keys; a split added for parallelism keeps at least
-    // kMinPrefillSplitKeys keys, and no split exceeds kMaxSplitKeys (its page
+    // min_keys keys, and no split exceeds kMaxSplitKeys (its page
     // ids are staged in LDS).
+    const int min_keys = s.dtype == kBf16 ? kMinPrefillSplitKeys : kMinPrefillSplitKeysF32;
     auto assign = [&](int64_t s_par) {
       int64_t tasks = 0;
       for (int k = 0; k < p.n; ++k) {
@@ -159,7 +160,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
         int64_t sp = 1;
         if (s_par > 1) {
           sp = (int64_t)std::floor((double)s_par * (double)tiles * ch.Lp / work);
-          sp = std::max<int64_t>(1, std::min<int64_t>(sp, ceil_div(ch.Lp, kMinPrefillSplitKeys)));
+          sp = std::max<int64_t>(1, std::min<int64_t>(sp, ceil_div(ch.Lp, min_keys)));
         }
         sp = std::max<int64_t>(sp, ceil_div(ch.Lp, kMaxSplitKeys));
         ch.split_keys = (int)round_up(ceil_div(ch.Lp, sp), bn);

@@ -27,7 +27,12 @@ constexpr int kSplitIdRegs = 4;         // page-id registers of a decode wave (6
 constexpr int kMaxSplitTokens = 64 * kPageSize * kSplitIdRegs;  // 4096 tokens per decode wave task
 constexpr int kMinSplitTokens = 256;
 constexpr int kMaxContext = 1023 * kMinSplitTokens;  // 261888 tokens: <= 1023 decode splits per request
+// Fewest keys a split added for parallelism keeps: a bf16 tile streams a
+// 64-key block in ~2.5 us, so shorter splits cost more in merges than they
+// gain; the fp32 tile (one row per lane on the vector unit) is ~30x slower
+// per key, so one 32-key block is worth a split.
 constexpr int kMinPrefillSplitKeys = 1024;
+constexpr int kMinPrefillSplitKeysF32 = 32;
 constexpr int kMaxSplitKeys = 16384;       // page ids of one split are staged in LDS
 constexpr int kShareDen = 64;
 constexpr int kMaxChunks = 16;             // prefill chunks of one call
