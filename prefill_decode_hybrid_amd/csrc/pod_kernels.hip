@@ -6,10 +6,11 @@
 // attention bandwidth-bound (paper abstract; §1), so one launch should run
 // both on every compute unit at once (§4).  A regular grid is launched and
 // every workgroup is remapped to a virtual prefill or decode workgroup
-// (§4.3); the choice is made after dispatch from a per-CU ticket, so each CU
-// receives both kinds in a fixed proportion (§4.1 SM-aware CTA scheduling,
-// §5.4.2 proportional allocation).  Decode work is cut into one-wave units
-// (§4.2.3 virtual decode CTAs).  Split partial results are merged by the
+// (§4.3); the choice is made after dispatch from what already runs on the
+// workgroup's compute unit (§4.1 SM-aware CTA scheduling: by default a
+// per-CU count of running prefill and decode workgroups against a prefill
+// target, or the per-CU ticket sequences of §5.4.2).  Decode work is cut
+// into one-wave units (§4.2.3 virtual decode CTAs).  Split partial results are merged by the
 // last split to arrive, so no workgroup ever waits for another (the Silicon
 // & Systems digest: results meet at synchronisation points and the
 // scheduler must not deadlock).

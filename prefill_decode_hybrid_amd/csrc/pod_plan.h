@@ -9,8 +9,10 @@
 //    at two full waves);
 //  * decode wave tasks (request, kv head, token split), one 64-lane wave each
 //    (paper §4.2.3, virtual decode CTAs of one warp), four per workgroup;
-//  * the fused launch's per-CU prefill share (paper §5.4.2: proportional
-//    allocation beats 50:50).
+//  * the fused launch's role mix: prefill workgroups kept per CU for the
+//    default CU-balanced policy (from the time each role needs alone), or
+//    the ticket share of the proportional and 50:50 policies (paper §5.4.2);
+//  * the chunk table when one call carries several prefill chunks.
 #pragma once
 
 #include <cstdint>
