@@ -106,8 +106,9 @@ typedef struct {
     int32_t prefill_slots_x256; /* CU-balanced policy: prefill workgroups kept running per
                                  CU, in 1/256 of a workgroup (1 .. 256 * wg_per_cu); 0
                                  selects the planner's choice from the batch            */
-    int32_t decode_split_tokens; /* tokens per decode wave task, a multiple of 16 in
-                                 256 .. 4096; 0 selects the planner's choice, which
+    int32_t decode_split_tokens; /* tokens per decode wave task, a multiple of 16 up to
+                                 4096 and at least 256 (bf16) or 64 (fp32) and
+                                 max_context / 1023; 0 selects the planner's choice, which
                                  depends on the decode batch alone (so a decode's result
                                  has the same bits in fused and decode-only launches)  */
     int32_t persistent;         /* 1: the fused launch is a resident grid (CUs x

@@ -50,7 +50,8 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   if (c->prefill_slots_x256 < 0 || c->prefill_slots_x256 > 2 * 256) return POD_ERR_INVALID_ARG;
   if (c->persistent != 0 && c->persistent != 1) return POD_ERR_INVALID_ARG;
   if (c->decode_split_tokens != 0 &&
-      (c->decode_split_tokens % pod::kPageSize != 0 || c->decode_split_tokens < pod::kMinSplitTokens ||
+      (c->decode_split_tokens % pod::kPageSize != 0 ||
+       c->decode_split_tokens < pod::min_split_tokens(s.dtype, c->max_context) ||
        c->decode_split_tokens > pod::kMaxSplitTokens))
     return POD_ERR_INVALID_ARG;
   lim.max_chunk_len = c->max_chunk_len;

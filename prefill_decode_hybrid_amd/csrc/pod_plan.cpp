@@ -49,7 +49,8 @@ void derive_capacities(const Shape& s, Limits& lim) {
        lim.cap_tiles * ceil_div(std::max(1, lim.max_context), kMaxSplitKeys)});
   int64_t total = lim.max_total_context > 0 ? lim.max_total_context
                                             : (int64_t)lim.max_num_decode * lim.max_context;
-  lim.cap_wave_tasks = (int64_t)s.hkv * (lim.max_num_decode + ceil_div(total, kMinSplitTokens));
+  lim.cap_wave_tasks =
+      (int64_t)s.hkv * (lim.max_num_decode + ceil_div(total, min_split_tokens(s.dtype, lim.max_context)));
 }
 
 WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim) {
@@ -258,7 +259,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     const int64_t median = lens[d.N / 2];
     const int64_t target = (int64_t)lim.num_cus * 5;
     int64_t T = round_up(std::min(ceil_div(pl.d_total * s.hkv, target), median), kPageSize);
-    T = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(kMinSplitTokens, T));
+    T = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(min_split_tokens(s.dtype, lim.max_context), T));
     if (lim.split_tokens > 0) T = lim.split_tokens;
     pl.T = (int)T;
     int64_t units = 0, full = 0;

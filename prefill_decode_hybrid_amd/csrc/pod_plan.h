@@ -28,7 +28,17 @@ constexpr int kWavesPerWG = 4;
 constexpr int kSplitIdRegs = 4;         // page-id registers of a decode wave (64 ids each)
 constexpr int kMaxSplitTokens = 64 * kPageSize * kSplitIdRegs;  // 4096 tokens per decode wave task
 constexpr int kMinSplitTokens = 256;
-constexpr int kMaxContext = 1023 * kMinSplitTokens;  // 261888 tokens: <= 1023 decode splits per request
+constexpr int kMinSplitTokensF32 = 64;  // the fp32 decode wave is latency-bound: shorter splits
+constexpr int kMaxSplitsPerRequest = 1023;  // the unit scan packs split counts in 10 bits
+constexpr int kMaxContext = kMaxSplitsPerRequest * kMinSplitTokens;  // 261888 tokens
+
+// Shortest decode split for `dtype` that keeps every context up to
+// `max_context` within kMaxSplitsPerRequest splits.
+inline int min_split_tokens(int dtype, int max_context) {
+  const int base = dtype == kBf16 ? kMinSplitTokens : kMinSplitTokensF32;
+  const int need = ((max_context + kMaxSplitsPerRequest - 1) / kMaxSplitsPerRequest + kPageSize - 1) / kPageSize * kPageSize;
+  return base > need ? base : need;
+}
 // Fewest keys a split added for parallelism keeps: a bf16 tile streams a
 // 64-key block in ~2.5 us, so shorter splits cost more in merges than they
 // gain; the fp32 tile (one row per lane on the vector unit) is ~30x slower

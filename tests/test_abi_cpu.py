@@ -95,7 +95,7 @@ def test_plan_invariants_on_configs(cid):
         assert st["prefill_tasks"] <= 2 * slots
     # decode: every (request, kv head) split into ceil(L / T) one-wave units
     T = st["decode_split_tokens"]
-    assert T % 16 == 0 and 256 <= T <= 4096
+    assert T % 16 == 0 and (256 if spec["dtype"] == "bf16" else 64) <= T <= 4096
     assert st["decode_wave_tasks"] == hkv * sum(-(-int(L) // T) for L in lens)
     assert st["decode_wg_tasks"] == -(-st["decode_wave_tasks"] // 4)
     assert st["grid"] == st["prefill_tasks"] + st["decode_wg_tasks"]
@@ -125,7 +125,7 @@ def test_forced_decode_split_tokens():
         st = plan(_cfg(3, decode_split_tokens=T), pod.MODE_HYBRID, _prefill(512, 1024), _decode(lens))
         assert st["decode_split_tokens"] == T
         assert st["decode_wave_tasks"] == 8 * sum(-(-L // T) for L in lens)
-    for bad in (100, 255, 4112, 1000, -16):
+    for bad in (100, 255, 4112, 1000, -16):  # bf16: multiples of 16 in 256 .. 4096
         with pytest.raises(pod.PodAttnError) as e:
             plan(_cfg(3, decode_split_tokens=bad), pod.MODE_DECODE, None, _decode(lens))
         assert e.value.status == pod.POD_ERR_INVALID_ARG
@@ -296,3 +296,16 @@ def test_persistent_plan():
     with pytest.raises(pod.PodAttnError) as e:
         plan(_cfg(3, persistent=2), pod.MODE_DECODE, None, _decode([5]))
     assert e.value.status == pod.POD_ERR_INVALID_ARG
+
+
+def test_fp32_decode_splits_and_the_split_limit():
+    # fp32 decode waves take splits down to 64 tokens, but never more than 1023 splits a request
+    cfg = _cfg(1, max_context=32768)
+    st = plan(cfg, pod.MODE_DECODE, None, _decode([37, 100, 256, 511]))
+    assert st["decode_split_tokens"] == 64
+    big = _cfg(1, max_context=200000, max_total_context=1 << 20)
+    st = plan(big, pod.MODE_DECODE, None, _decode([37, 511]))
+    assert st["decode_split_tokens"] >= -(-200000 // 1023)
+    with pytest.raises(pod.PodAttnError):
+        plan(_cfg(1, max_context=200000, decode_split_tokens=64), pod.MODE_DECODE, None, _decode([37]))
+    assert plan(_cfg(1, decode_split_tokens=64), pod.MODE_DECODE, None, _decode([37]))["decode_split_tokens"] == 64
