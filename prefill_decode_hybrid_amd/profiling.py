@@ -10,6 +10,12 @@ the kernels: true bytes = counter * (copy bytes / counter value of the copy).
 
     python -m prefill_decode_hybrid_amd.profiling --workload NAME \
         --trace DIR --fetch DIR --write DIR --out profiles/
+
+A second mode summarises SQ counter passes (instruction mix, MFMA busy
+cycles, LDS bank conflicts, waits) per kernel:
+
+    python -m prefill_decode_hybrid_amd.profiling counters --workload NAME \
+        --pmc DIR [DIR ...] --out profiles/
 """
 from __future__ import annotations
 
@@ -87,7 +93,77 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
     return out
 
 
+SIMDS = 256 * 4       # MI355X: 256 compute units of 4 SIMDs
+CLOCK_HZ = 2.4e9      # peak engine clock
+RATIOS = [  # (label, numerator, denominator): definitions that need no per-chip normalisation
+    ("vector instructions per MFMA", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
+    ("exp/transcendental instructions per MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA"),
+    ("LDS instructions per MFMA", "SQ_INSTS_LDS", "SQ_INSTS_MFMA"),
+    ("scalar instructions per MFMA", "SQ_INSTS_SALU", "SQ_INSTS_MFMA"),
+    ("MFMA busy cycles per MFMA instruction", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA"),
+    ("LDS bank-conflict cycles per LDS-active cycle", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+    ("share of wave time waiting on s_waitcnt", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+]
+
+
+def counters_main(argv):
+    """Summary of SQ counter passes: mean value per dispatch for every pod kernel."""
+    ap = argparse.ArgumentParser(prog="profiling counters")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--pmc", nargs="+", required=True, help="rocprofv3 --pmc output directories")
+    ap.add_argument("--out", default="profiles")
+    ap.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    vals = defaultdict(lambda: defaultdict(list))
+    for d in a.pmc:
+        for r in _rows(d, "counter_collection.csv"):
+            k = short_name(r["Kernel_Name"])
+            if k.startswith("pod_"):
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for v in vals.values() for c in v})
+    kernels = sorted(vals)
+    lines = [f"# rocprofv3 counters: {a.workload}", "", f"kernel sources: `{kernel_sources_hash()}`", ""]
+    if a.command:
+        lines += ["Commands:", "", "```", a.command, "```", ""]
+    lines += ["Mean value per dispatch (counters summed over the chip by rocprofv3).", "",
+              "| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |",
+              "|---|" + "---|" * len(kernels)]
+    mean = {k: {c: statistics.mean(v) for c, v in vals[k].items()} for k in kernels}
+    for c in names:
+        lines.append(f"| {c} | " + " | ".join(f"{mean[k][c]:.4g}" if c in mean[k] else "" for k in kernels) + " |")
+    lines += ["", "| ratio | " + " | ".join(f"`{k}`" for k in kernels) + " |", "|---|" + "---|" * len(kernels)]
+    for label, num, den in RATIOS:
+        cells = []
+        for k in kernels:
+            m = mean[k]
+            cells.append(f"{m[num] / m[den]:.3g}" if num in m and den in m and m[den] else "")
+        lines.append(f"| {label} | " + " | ".join(cells) + " |")
+    # durations of the same dispatches, when the passes also ran --kernel-trace
+    dur = defaultdict(list)
+    for d in a.pmc:
+        for r in _rows(d, "kernel_trace.csv"):
+            k = short_name(r["Kernel_Name"])
+            if k in mean:
+                dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if dur:
+        lines.append("| mean duration in these runs (us) | " +
+                     " | ".join(f"{statistics.mean(dur[k]):.1f}" if dur[k] else "" for k in kernels) + " |")
+        cells = []
+        for k in kernels:
+            m = mean[k]
+            ok = dur[k] and "SQ_VALU_MFMA_BUSY_CYCLES" in m
+            cells.append(f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * statistics.mean(dur[k]) * 1e-6 * CLOCK_HZ):.3f}"
+                         if ok else "")
+        lines.append(f"| MFMA busy share ({SIMDS} SIMDs at {CLOCK_HZ / 1e9:.1f} GHz) | " + " | ".join(cells) + " |")
+    os.makedirs(a.out, exist_ok=True)
+    open(os.path.join(a.out, f"counters_{a.workload}.md"), "w").write("\n".join(lines) + "\n")
+    print(json.dumps({"workload": a.workload, "kernels": kernels, "counters": names}))
+
+
 def main():
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        return counters_main(sys.argv[2:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--trace", required=True)
