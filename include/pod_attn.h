@@ -143,7 +143,7 @@ typedef struct {
  * 0 .. chunk_offsets[c] + i of its own page table (row c of page_table).
  * The sum of the chunk lengths must not exceed max_chunk_len of the config.
  * With one chunk the result equals pod_attn_hybrid's bit for bit. */
-#define POD_MAX_CHUNKS 16
+#define POD_MAX_CHUNKS 64
 typedef struct {
     const void *q;              /* device [sum of chunk_lens, Hq, head_dim]            */
     void *o;                    /* device [sum of chunk_lens, Hq, head_dim]            */

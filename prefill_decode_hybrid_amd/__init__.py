@@ -23,7 +23,7 @@ POD_BF16, POD_F32 = 0, 1
 POD_POLICY_CU_BALANCED, POD_POLICY_PROPORTIONAL, POD_POLICY_HALF, POD_POLICY_STATIC = 0, 1, 2, 3
 MODE_HYBRID, MODE_PREFILL, MODE_DECODE = 0, 1, 2
 
-POD_MAX_CHUNKS = 16
+POD_MAX_CHUNKS = 64
 
 EXPORTED = ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_prefill_only",
             "pod_attn_decode_only", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",

@@ -887,15 +887,25 @@ DEV PfChunk load_chunk(int c) {
   return r;
 }
 
+DEV int chunk_task_base(int c) {
+  return ((karg_chunk_t*)((karg_char_t*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(PodParams, ch)) + c)
+      ->task_base;
+}
+
 template <int RPW>
 DEV TaskGeom prefill_geom(const PodParams& p, int task) {
   TaskGeom t;
   task = __builtin_amdgcn_readfirstlane(task);
-  int c = 0;  // the last chunk whose first task is <= task
-#pragma unroll
-  for (int k = 1; k < kMaxChunks; ++k)
-    if (k < p.n_chunks && task >= p.ch[k].task_base) c = k;
-  const PfChunk ch = load_chunk(c);
+  // the last chunk whose first task is <= task (binary search, scalar loads)
+  int lo = 0, hi = p.n_chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (task >= chunk_task_base(mid))
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const PfChunk ch = load_chunk(lo);
   t.C = ch.C;
   t.P0 = ch.P0;
   t.Lp = ch.C + ch.P0;

@@ -54,6 +54,10 @@ struct PodParams {
   int share_num, share_den, cu_prefill_x256, policy, grid;
 };
 
+// The parameter block is the kernels' only argument (kernel arguments are
+// limited to 4 KiB).
+static_assert(sizeof(PodParams) <= 4096, "kernel argument block");
+
 enum { kKernelHybrid = 0, kKernelPrefill = 1, kKernelDecode = 2 };
 
 // Launch one kernel for `which` with geometry from `pl`.  Returns a hipError_t.

@@ -47,7 +47,7 @@ constexpr int kMinPrefillSplitKeys = 1024;
 constexpr int kMinPrefillSplitKeysF32 = 32;
 constexpr int kMaxSplitKeys = 16384;       // page ids of one split are staged in LDS
 constexpr int kShareDen = 64;
-constexpr int kMaxChunks = 16;             // prefill chunks of one call
+constexpr int kMaxChunks = 64;             // prefill chunks of one call (the table travels in the kernel arguments)
 // Throughput of the split kernels on MI355X, used only to pick the fused
 // launch's per-CU prefill slots: prefill FLOP/s (bf16 and fp32 tiles) and
 // decode bytes/s over the whole chip, and the decode time below which a

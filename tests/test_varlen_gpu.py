@@ -44,6 +44,12 @@ CASES = [
     vspec("bf16", 16, 2, 128, [(16 + i, 97 * i) for i in range(16)], [900, 2]),
     vspec("bf16", 8, 8, 128, [(300, 20000), (31, 0)], [5, 40000]),
     vspec("f32", 8, 2, 64, [(100, 29), (3, 3000), (64, 0)], [3, 999]),
+    # the chunk limit: 64 single-row chunks
+    vspec("bf16", 8, 2, 128, [(1, 100 * i) for i in range(64)], [77]),
+    # multi-token decode queries (3 new tokens each, contexts 1-16K) passed as chunks
+    # of 3 rows at offset L - 3, beside one prompt chunk and single-token decodes
+    vspec("bf16", 32, 8, 128, [(256, 0)] + [(3, 1000 + (997 * i) % 15000 - 3) for i in range(47)],
+          [16384, 4096, 9]),
 ]
 
 
