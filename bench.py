@@ -55,13 +55,14 @@ def work_counts(b):
 
 def load_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None if
-    they are missing or were taken on different kernel sources."""
+    they are missing or were taken on different kernel machine code."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    from prefill_decode_hybrid_amd.profiling import kernel_sources_hash
-    if t.get("kernel_sources") != kernel_sources_hash():
+    from prefill_decode_hybrid_amd.profiling import kernel_code_hash
+    code = kernel_code_hash()
+    if code is None or t.get("kernel_code") != code:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -177,7 +178,7 @@ def main():
     import torch
     import prefill_decode_hybrid_amd as pod
     from prefill_decode_hybrid_amd import inputs
-    from prefill_decode_hybrid_amd.profiling import kernel_sources_hash
+    from prefill_decode_hybrid_amd.profiling import kernel_code_hash
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -319,7 +320,7 @@ def main():
         "finite": finite,
         "plan": plan,
         "gpu": torch.cuda.get_device_name(0),
-        "kernel_sources": kernel_sources_hash(),
+        "kernel_code": kernel_code_hash(),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")

@@ -148,17 +148,6 @@ DEV void store_out(void* base, int64_t idx, float v) {
   }
 }
 
-DEV float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-DEV float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
 // Split partials cross compute units on different XCDs, whose L2s are not
 // coherent with each other.  They are written and read with device-scope
 // accesses (cache policy sc1: written through to, and read from, the device

@@ -26,6 +26,7 @@ import hashlib
 import json
 import os
 import statistics
+import struct
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,14 +34,33 @@ CALIB_BYTES = 512 << 20          # the counter workload's device copy (read and 
 CALIB_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def kernel_sources_hash() -> str:
-    """Hash of the HIP/C++ sources: counter data is tied to the code it measured."""
-    h = hashlib.sha256()
-    csrc = os.path.join(HERE, "csrc")
-    for fn in sorted(os.listdir(csrc)):
-        if fn.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, fn), "rb").read())
-    return h.hexdigest()[:16]
+def _elf_section(path: str, name: str):
+    """Bytes of section `name` of a 64-bit little-endian ELF file, or None."""
+    b = open(path, "rb").read()
+    if b[:4] != b"\x7fELF" or b[4] != 2:
+        return None
+    shoff, = struct.unpack_from("<Q", b, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+
+    def header(i):
+        return struct.unpack_from("<IIQQQQ", b, shoff + i * shentsize)
+
+    names = header(shstrndx)[4]
+    for i in range(shnum):
+        nm, _, _, _, off, size = header(i)
+        if b[names + nm: b.index(b"\0", names + nm)].decode() == name:
+            return b[off: off + size]
+    return None
+
+
+def kernel_code_hash(lib: str = os.path.join(HERE, "libpodattn.so")):
+    """Hash of the library's GPU code objects (its .hip_fatbin section): counter
+    data is tied to the machine code it measured, and edits that leave the
+    code unchanged (comments) keep it."""
+    if not os.path.exists(lib):
+        return None
+    code = _elf_section(lib, ".hip_fatbin")
+    return None if code is None else hashlib.sha256(code).hexdigest()[:16]
 
 
 def short_name(name: str) -> str:
@@ -122,7 +142,7 @@ def counters_main(argv):
                 vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
     names = sorted({c for v in vals.values() for c in v})
     kernels = sorted(vals)
-    lines = [f"# rocprofv3 counters: {a.workload}", "", f"kernel sources: `{kernel_sources_hash()}`", ""]
+    lines = [f"# rocprofv3 counters: {a.workload}", "", f"kernel code objects: `{kernel_code_hash()}`", ""]
     if a.command:
         lines += ["Commands:", "", "```", a.command, "```", ""]
     lines += ["Mean value per dispatch (counters summed over the chip by rocprofv3).", "",
@@ -174,16 +194,16 @@ def main():
     a = ap.parse_args()
     dur = kernel_durations(a.trace)
     tr = traffic(a.fetch, a.write)
-    src = kernel_sources_hash()
+    src = kernel_code_hash()
     hybrid = next((k for k in tr["kernels"] if k.startswith("pod_hybrid_kernel")), None)
-    rec = {"workload": a.workload, "kernel_sources": src, "kernel": hybrid,
+    rec = {"workload": a.workload, "kernel_code": src, "kernel": hybrid,
            "hbm_bytes_per_launch": tr["kernels"][hybrid]["hbm_bytes"] if hybrid else None,
            "calibration": {"copy_bytes": CALIB_BYTES, "fetch_bytes_per_kib": tr["fetch_bytes_per_kib"],
                            "write_bytes_per_kib": tr["write_bytes_per_kib"]},
            "kernels": tr["kernels"]}
     os.makedirs(a.out, exist_ok=True)
     json.dump(rec, open(os.path.join(a.out, f"traffic_{a.workload}.json"), "w"), indent=1)
-    lines = [f"# rocprofv3 summary: {a.workload}", "", f"kernel sources: `{src}`", ""]
+    lines = [f"# rocprofv3 summary: {a.workload}", "", f"kernel code objects: `{src}`", ""]
     if a.command:
         lines += ["Commands:", "", "```", a.command, "```", ""]
     lines += ["| kernel | calls | mean us | median us | min us | HBM read MB | HBM write MB |",
