@@ -62,3 +62,12 @@ def test_counters_mode(tmp_path, capsys):
     assert "| MFMA busy cycles per MFMA instruction | 32 |" in md
     assert "| LDS bank-conflict cycles per LDS-active cycle | 0 |" in md
     assert f"| {3200 / (1024 * 1e-6 * 2.4e9):.3f} |" in md
+
+
+def test_kernel_code_hash(tmp_path):
+    h = profiling.kernel_code_hash()
+    assert h is not None and len(h) == 16 and int(h, 16) >= 0
+    assert profiling.kernel_code_hash(str(tmp_path / "missing.so")) is None
+    junk = tmp_path / "junk.so"
+    junk.write_bytes(b"not an ELF file")
+    assert profiling.kernel_code_hash(str(junk)) is None
