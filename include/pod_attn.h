@@ -179,6 +179,8 @@ typedef struct {
     int32_t policy;
     int32_t prefill_chunks;     /* prefill chunks of the call (0 without prefill)     */
     int32_t persistent;         /* 1 if the fused launch ran as a resident grid       */
+    int32_t decode_first;       /* 1 if the fused launch handed the decode tasks to the
+                                   first workgroup ids (decode first, one round)      */
 } pod_attn_stats;
 
 /* Validate `cfg`, pick the device, reserve the workspace.  Returns POD_OK and

@@ -65,7 +65,8 @@ class PodAttnStats(ctypes.Structure):
         "mode", "fallback", "num_cus", "wg_per_cu", "grid", "prefill_rows_per_tile",
         "prefill_heads_per_tile", "prefill_tiles", "prefill_splits", "prefill_split_keys",
         "prefill_tasks", "decode_split_tokens", "decode_wave_tasks", "decode_wg_tasks",
-        "share_num", "share_den", "cu_prefill_x256", "policy", "prefill_chunks", "persistent")]
+        "share_num", "share_den", "cu_prefill_x256", "policy", "prefill_chunks", "persistent",
+        "decode_first")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

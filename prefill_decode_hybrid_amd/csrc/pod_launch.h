@@ -52,6 +52,7 @@ struct PodParams {
   uint32_t* ctrl_next;  // the other block, cleared by this launch for the next one
   uint32_t* tickets;  // per-CU words: ticket counters, or running prefill | decode << 16
   int share_num, share_den, cu_prefill_x256, policy, grid;
+  int decode_first;  // fused launch: the first d_wg_tasks workgroup ids run the decode tasks
 };
 
 // The parameter block is the kernels' only argument (kernel arguments are

@@ -275,6 +275,12 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   }
 
   pl.grid = (pl.has_p ? pl.p_tasks : 0) + (pl.has_d ? pl.d_wg_tasks : 0);
+  // Decode first with every decode workgroup resident at once: handing the
+  // decode tasks to the first workgroup ids runs the same schedule as the
+  // claims without their atomics in front of the work (a decode of several
+  // rounds keeps the claims, which balance the XCDs).
+  pl.decode_first = pl.has_p && pl.has_d && !lim.persistent && lim.policy == kPolicyCuBalanced &&
+                    pl.cu_prefill_x256 == 0 && pl.d_wg_tasks <= slots;
   if (pl.has_p && pl.has_d && lim.persistent) {
     pl.persistent = true;  // every resident slot loops over the queues
     pl.grid = (int)std::min<int64_t>(pl.grid, slots);

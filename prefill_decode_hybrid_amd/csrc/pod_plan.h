@@ -114,6 +114,7 @@ struct Plan {
   // fused scheduling
   int share_num = 0, share_den = 1, cu_prefill_x256 = 0, policy = 0;
   bool persistent = false;  // the fused launch is a resident grid of workgroups
+  bool decode_first = false;  // decode tasks by workgroup id first, then prefill (no claims)
 };
 
 // Rows of one wave's query block and keys per staged KV block, per dtype.

@@ -146,3 +146,19 @@ def test_config_sampled(cid):
     assert torch.isfinite(op.float()).all() and torch.isfinite(od.float()).all()
     sp_, sd_ = run.separate()
     assert torch.equal(op, sp_) and torch.equal(od, sd_), "fused result differs from split launches"
+
+
+def test_decode_first_by_workgroup_id():
+    # a short chunk beside longer decodes: decode first, all decode workgroups in one round
+    sp = spec("bf16", 8, 2, 128, 32, 0, [8192] * 16 + [3, 700])
+    run = Run(inputs.make_batch(sp, seed=11))
+    try:
+        op, od = run.hybrid()
+        st = run.att.stats()
+        say(f"decode first plan {st}")
+        assert st["decode_first"] == 1 and st["cu_prefill_x256"] == 0
+        check_against_oracle(run, op, od, label="decode first")
+        sp_, sd_ = run.separate()
+        assert torch.equal(op, sp_) and torch.equal(od, sd_)
+    finally:
+        run.close()
