@@ -43,6 +43,8 @@ def main(argv=None):
     ap.add_argument("--num-kv-heads", type=int, default=8)
     ap.add_argument("--head-dim", type=int, default=128)
     ap.add_argument("--policy", type=int, default=0)
+    ap.add_argument("--slots-x256", type=int, default=0,
+                    help="CU-balanced policy: prefill workgroups per CU in 1/256 (0: the planner's choice)")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
@@ -63,7 +65,7 @@ def main(argv=None):
     b = inputs.make_batch(spec, seed=a.seed)
     dev = b.to("cuda:0")
     ctx = b.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(b, policy=a.policy))
+    att = pod.PodAttention(pod.config_for_batch(b, policy=a.policy, prefill_slots_x256=a.slots_x256))
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     op, od = torch.empty_like(dev.q_prefill), torch.empty_like(dev.q_decode)
@@ -93,7 +95,7 @@ def main(argv=None):
     t_roof = max(flops / PEAK_BF16_FLOPS, nbytes / PEAK_HBM) * 1e6
     out = {"batch": "several prefill chunks beside a decode batch", "chunks": chunks,
            "num_decode": a.num_decode, "decode_context": a.decode_context, "heads": [hq, hkv], "head_dim": d,
-           "policy": a.policy, "steps": a.steps, "fused_us": round(t_f, 1), "serial_us": round(t_s, 1),
+           "policy": a.policy, "slots_x256": a.slots_x256, "steps": a.steps, "fused_us": round(t_f, 1), "serial_us": round(t_s, 1),
            "two_stream_us": round(t_2, 1), "speedup_vs_serial": round(t_s / t_f, 4),
            "speedup_vs_two_stream": round(t_2 / t_f, 4),
            "overlap_roofline": {"t_roof_us": round(t_roof, 1), "frac": round(t_roof / t_f, 4),
