@@ -23,7 +23,6 @@ struct pod_attn_handle {
   pod::WorkspaceLayout lay;
   pod_attn_stats stats{};
   char err[256] = {0};
-  uint32_t fused_launches = 0;  // picks the fused launch's control block (parity)
 };
 
 namespace {
@@ -172,8 +171,7 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
   p.hkv = s.hkv;
   p.scale_log2 = h->sm_scale * 1.4426950408889634f;
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(h->ws + h->lay.ctrl);
-  p.ctrl = ctrl + pod::kCtrlBlock * (h->fused_launches & 1u);
-  p.ctrl_next = ctrl + pod::kCtrlBlock * ((h->fused_launches + 1u) & 1u);
+  p.ctrl = ctrl;
   p.tickets = reinterpret_cast<uint32_t*>(h->ws + h->lay.tickets);
   p.p_cnt = reinterpret_cast<uint32_t*>(h->ws + h->lay.p_cnt);
   p.d_cnt = reinterpret_cast<uint32_t*>(h->ws + h->lay.d_cnt);
@@ -223,7 +221,6 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
   if (pl.grid > 0) {
     e = (hipError_t)pod::launch(which, s.dtype, s.d, s.G, p, pl, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
-    if (which == pod::kKernelHybrid) ++h->fused_launches;  // the next one runs on the cleared block
   }
   fill_stats(pl, &h->stats);
   return POD_OK;

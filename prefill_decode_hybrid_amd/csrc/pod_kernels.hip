@@ -1548,9 +1548,17 @@ DEV void pick_and_claim(const PodParams& p, int& role, int& task, bool& counted,
   }
 }
 
-DEV void clear_next_ctrl(const PodParams& p) {
-  for (int q = 0; q < kCtrlUsed; ++q)
-    __hip_atomic_store(p.ctrl_next + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Thread 0 of a workgroup that is done claiming: count it out; the last of
+// the launch's workgroups clears the control words for the next launch.
+// Every claim is a returning device-scope atomic and the flag stores are
+// complete (vmcnt 0) before the count, so the clear lands after all of them
+// without cache maintenance (an acquire-release count here, which writes
+// back and invalidates the L2, made the fused launch 3-7% slower).
+DEV void leave_claims(const PodParams& p) {
+  wait_vmem();
+  const uint32_t n = __hip_atomic_fetch_add(p.ctrl + kCtrlExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (n == (uint32_t)p.grid - 1u)
+    for (int q = 0; q < kCtrlUsed; ++q) __hip_atomic_store(p.ctrl + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Fused hybrid kernel.  A regular grid of prefill tasks + decode workgroup
@@ -1589,10 +1597,8 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
       task = role == 1 ? (int)blockIdx.x : (int)blockIdx.x - p.d_wg_tasks;
     } else {
       pick_and_claim(p, role, task, counted, key);
+      leave_claims(p);  // one claim per workgroup
     }
-    // The previous launch on this handle used the other block and has
-    // finished (stream order); clear it for the next launch.
-    if (blockIdx.x == 0) clear_next_ctrl(p);
     cu_word = key;
     role_task[0] = role;
     role_task[1] = task;
@@ -1620,13 +1626,13 @@ __global__ __launch_bounds__(256, 2) void pod_persistent_kernel(PodParams p) {
   POD_DECLARE_LDS(E, D);
   __shared__ int role_task[3];
   __shared__ uint32_t cu_word;
-  if (blockIdx.x == 0 && threadIdx.x == 0) clear_next_ctrl(p);
   while (true) {
     if (threadIdx.x == 0) {
       int role, task = 0;
       bool counted;
       uint32_t key;
       pick_and_claim(p, role, task, counted, key);
+      if (task >= (role == 0 ? p.p_tasks : p.d_wg_tasks)) leave_claims(p);  // both queues empty
       cu_word = key;
       role_task[0] = role;
       role_task[1] = task;

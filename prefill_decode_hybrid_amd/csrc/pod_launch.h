@@ -48,8 +48,7 @@ struct PodParams {
   uint32_t* d_cnt;   // [request][kv head] arrival counters, 0 between calls
 
   // fused launch
-  uint32_t* ctrl;     // this launch's control block (pod_plan.h kCtrl*)
-  uint32_t* ctrl_next;  // the other block, cleared by this launch for the next one
+  uint32_t* ctrl;     // control words (pod_plan.h kCtrl*), zero at launch, left zero
   uint32_t* tickets;  // per-CU words: ticket counters, or running prefill | decode << 16
   int share_num, share_den, cu_prefill_x256, policy, grid;
   int decode_first;  // fused launch: the first d_wg_tasks workgroup ids run the decode tasks

@@ -139,15 +139,16 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p,
 constexpr int kTicketSlots = 2048;  // (xcc, se, sh, cu) keys
 constexpr int kCtrlWords = 64;
 constexpr int kXcdQueues = 8;         // per-XCD task queues (queue x holds tasks x, x+8, ...)
-// Fused-launch control words.  Two blocks of kCtrlBlock words alternate
-// between consecutive launches on a handle: a launch runs on block
-// (launch count & 1) and clears the other block for the launch after it.
-constexpr int kCtrlBlock = 32;
+// Fused-launch control words.  Each workgroup of a launch whose roles are
+// claimed counts itself out (kCtrlExit) after its last claim; the last one
+// out clears the words, so every launch -- also a replay of a captured
+// graph -- starts on clean words, with no host-side state.
 constexpr int kCtrlPrefillHeads = 0;  // [0..7] prefill queue heads
 constexpr int kCtrlDecodeHeads = 8;   // [8..15] decode workgroup-task queue heads
 constexpr int kCtrlPrefillDone = 16;  // set once a claim found every prefill queue empty
 constexpr int kCtrlDecodeDone = 17;   // set once a claim found every decode queue empty
-constexpr int kCtrlUsed = 18;         // words of a block that a launch may dirty
-static_assert(2 * kCtrlBlock <= kCtrlWords, "control blocks");
+constexpr int kCtrlExit = 18;         // workgroups done claiming
+constexpr int kCtrlUsed = 19;         // words a launch may dirty
+static_assert(kCtrlUsed <= kCtrlWords, "control words");
 
 }  // namespace pod

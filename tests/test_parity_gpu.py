@@ -162,3 +162,40 @@ def test_decode_first_by_workgroup_id():
         assert torch.equal(op, sp_) and torch.equal(od, sd_)
     finally:
         run.close()
+
+
+@pytest.mark.parametrize("persistent", [0, 1])
+def test_fused_launch_in_a_captured_graph(persistent):
+    # the control words are restored by the launch itself, so replays of a
+    # captured launch (with eager work in between) give the eager result every time
+    run = Run(inputs.make_batch(SMALL[4], seed=12), persistent=persistent)
+    try:
+        ref = run.hybrid()
+        st = run.att.stats()
+        assert st["decode_first"] == 0 and st["policy"] == pod.POD_POLICY_CU_BALANCED  # roles are claimed
+        assert st["persistent"] == persistent
+        op, od = run.outputs()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run.att.hybrid(run.dev, op, od, run.ctx_host)  # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run.att.hybrid(run.dev, op, od, run.ctx_host)
+        scratch = torch.zeros(1 << 20, device="cuda:0")
+        for i in range(4):
+            op.fill_(float("nan"))
+            od.fill_(float("nan"))
+            scratch.add_(1.0)  # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            say(f"replay {i}")
+            assert torch.equal(op, ref[0]) and torch.equal(od, ref[1]), f"replay {i} differs from the eager launch"
+        # and an eager launch after the replays still matches
+        op2, od2 = run.hybrid()
+        assert torch.equal(op2, ref[0]) and torch.equal(od2, ref[1])
+    finally:
+        run.close()
