@@ -49,6 +49,12 @@
  * pod_attn_decode_only use disjoint workspace, so one of each may run at the
  * same time on two streams; two concurrent calls of the same entry point,
  * or a hybrid call concurrent with anything else, on one handle race.
+ *
+ * Graphs: a compute call enqueues exactly one kernel launch and no memset or
+ * copy, and every launch leaves the workspace's counters and control words
+ * as it found them (zero), with no host-side state between calls; a call
+ * may therefore be captured into a HIP graph and replayed, provided the
+ * batch shape (which sizes the launch on the host) stays the one captured.
  */
 #ifndef POD_ATTN_H
 #define POD_ATTN_H
