@@ -197,5 +197,16 @@ def test_fused_launch_in_a_captured_graph(persistent):
         # and an eager launch after the replays still matches
         op2, od2 = run.hybrid()
         assert torch.equal(op2, ref[0]) and torch.equal(od2, ref[1])
+        # the split launches (their merge counters are restored by the last arriver)
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            run.att.prefill_only(run.dev, op)
+            run.att.decode_only(run.dev, od, run.ctx_host)
+        for i in range(3):
+            op.fill_(float("nan"))
+            od.fill_(float("nan"))
+            g2.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(op, ref[0]) and torch.equal(od, ref[1]), f"split replay {i} differs"
     finally:
         run.close()
