@@ -185,8 +185,9 @@ typedef struct {
     int32_t policy;
     int32_t prefill_chunks;     /* prefill chunks of the call (0 without prefill)     */
     int32_t persistent;         /* 1 if the fused launch ran as a resident grid       */
-    int32_t decode_first;       /* 1 if the fused launch handed the decode tasks to the
-                                   first workgroup ids (decode first, one round)      */
+    int32_t fixed_order;        /* fused launch: 0 roles claimed after dispatch; 1 / 2
+                                   the prefill / decode tasks went to the first
+                                   workgroup ids (a launch resident in one round)     */
 } pod_attn_stats;
 
 /* Validate `cfg`, pick the device, reserve the workspace.  Returns POD_OK and

@@ -79,7 +79,7 @@ void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
   st->prefill_tiles = pl.tiles;
   st->prefill_chunks = pl.has_p ? pl.n_chunks : 0;
   st->persistent = pl.persistent ? 1 : 0;
-  st->decode_first = pl.decode_first ? 1 : 0;
+  st->fixed_order = pl.fixed_order;
   st->prefill_splits = pl.has_p ? pl.ch[0].splits : 0;
   st->prefill_split_keys = pl.has_p ? pl.ch[0].split_keys : 0;
   st->prefill_tasks = pl.has_p ? pl.p_tasks : 0;
@@ -209,7 +209,7 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
   p.share_den = pl.share_den;
   p.cu_prefill_x256 = pl.cu_prefill_x256;
   p.policy = pl.policy;
-  p.decode_first = pl.decode_first ? 1 : 0;
+  p.fixed_order = pl.fixed_order;
   p.grid = pl.grid;
 
   int which = pod::kKernelHybrid;

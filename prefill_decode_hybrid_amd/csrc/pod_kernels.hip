@@ -1577,9 +1577,9 @@ DEV void leave_claims(const PodParams& p) {
 //     runs prefill for share_num of every share_den arrivals, prefill first
 //     (paper §5.4.2).
 //   static: workgroup id decides, without looking at the CU (paper §3.3).
-// A CU-balanced mix with no prefill slots whose decode fits in one round of
-// resident workgroups (decode_first) also hands out roles by workgroup id:
-// decode tasks first, then prefill, with no atomics in front of the work.
+// A CU-balanced launch resident in one round (fixed_order) also hands out
+// roles by workgroup id -- one role's tasks first, then the other's -- with
+// no atomics in front of the work.
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   POD_DECLARE_LDS(E, D);
@@ -1592,9 +1592,11 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
     if (p.policy == kPolicyStatic) {
       role = (int)blockIdx.x < p.p_tasks ? 0 : 1;
       task = role == 0 ? (int)blockIdx.x : (int)blockIdx.x - p.p_tasks;
-    } else if (p.decode_first) {
-      role = (int)blockIdx.x < p.d_wg_tasks ? 1 : 0;
-      task = role == 1 ? (int)blockIdx.x : (int)blockIdx.x - p.d_wg_tasks;
+    } else if (p.fixed_order) {
+      const int first = p.fixed_order == 2 ? 1 : 0;
+      const int n_first = first == 1 ? p.d_wg_tasks : p.p_tasks;
+      role = (int)blockIdx.x < n_first ? first : 1 - first;
+      task = role == first ? (int)blockIdx.x : (int)blockIdx.x - n_first;
     } else {
       pick_and_claim(p, role, task, counted, key);
       leave_claims(p);  // one claim per workgroup

@@ -51,7 +51,7 @@ struct PodParams {
   uint32_t* ctrl;     // control words (pod_plan.h kCtrl*), zero at launch, left zero
   uint32_t* tickets;  // per-CU words: ticket counters, or running prefill | decode << 16
   int share_num, share_den, cu_prefill_x256, policy, grid;
-  int decode_first;  // fused launch: the first d_wg_tasks workgroup ids run the decode tasks
+  int fixed_order;   // fused launch: 1 / 2 = the first workgroup ids run the prefill / decode tasks
 };
 
 // The parameter block is the kernels' only argument (kernel arguments are

@@ -275,12 +275,18 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   }
 
   pl.grid = (pl.has_p ? pl.p_tasks : 0) + (pl.has_d ? pl.d_wg_tasks : 0);
-  // Decode first with every decode workgroup resident at once: handing the
-  // decode tasks to the first workgroup ids runs the same schedule as the
-  // claims without their atomics in front of the work (a decode of several
-  // rounds keeps the claims, which balance the XCDs).
-  pl.decode_first = pl.has_p && pl.has_d && !lim.persistent && lim.policy == kPolicyCuBalanced &&
-                    pl.cu_prefill_x256 == 0 && pl.d_wg_tasks <= slots;
+  // Roles by workgroup id instead of claims, when that runs the same
+  // schedule without the claims' atomics in front of the work: decode first
+  // with every decode workgroup resident at once, or a launch whose whole
+  // grid is resident at once (prefill first: the dispatcher spreads the
+  // first workgroup ids over the CUs).  Launches of several rounds keep the
+  // claims, which balance the CUs and XCDs as workgroups come and go.
+  if (pl.has_p && pl.has_d && !lim.persistent && lim.policy == kPolicyCuBalanced) {
+    if (pl.cu_prefill_x256 == 0 && pl.d_wg_tasks <= slots)
+      pl.fixed_order = 2;
+    else if (pl.grid <= slots)
+      pl.fixed_order = 1;
+  }
   if (pl.has_p && pl.has_d && lim.persistent) {
     pl.persistent = true;  // every resident slot loops over the queues
     pl.grid = (int)std::min<int64_t>(pl.grid, slots);

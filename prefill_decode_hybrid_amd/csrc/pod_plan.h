@@ -114,7 +114,7 @@ struct Plan {
   // fused scheduling
   int share_num = 0, share_den = 1, cu_prefill_x256 = 0, policy = 0;
   bool persistent = false;  // the fused launch is a resident grid of workgroups
-  bool decode_first = false;  // decode tasks by workgroup id first, then prefill (no claims)
+  int fixed_order = 0;  // 0: roles claimed; 1 / 2: prefill / decode tasks by workgroup id first (no claims)
 };
 
 // Rows of one wave's query block and keys per staged KV block, per dtype.

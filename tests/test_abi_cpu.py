@@ -149,19 +149,29 @@ def test_role_mix_by_work_ratio(P0, x):
     st = plan(_cfg(3), pod.MODE_HYBRID, _prefill(C, P0), _decode([16384] * 64))
     assert st["cu_prefill_x256"] == x
     # decode first in one round of resident workgroups: roles by workgroup id
-    assert st["decode_first"] == (1 if x == 0 else 0)
+    assert st["fixed_order"] == (2 if x == 0 else 0)
     assert st["decode_wg_tasks"] <= 256 * st["wg_per_cu"]
 
 
-def test_decode_first_by_id_only_for_one_round():
+def test_fixed_order_only_for_one_round():
     # the decode-heavy batch runs decode first over several rounds: claims stay
     spec = inputs.CONFIGS[4]
     st = plan(_cfg(4), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
               _decode(inputs.draw_context_lens(4, 0)))
-    assert st["cu_prefill_x256"] == 0 and st["decode_wg_tasks"] > 512 and st["decode_first"] == 0
+    assert st["cu_prefill_x256"] == 0 and st["decode_wg_tasks"] > 512 and st["fixed_order"] == 0
     for kw in (dict(persistent=1), dict(policy=pod.POD_POLICY_PROPORTIONAL)):
         st = plan(_cfg(3, **kw), pod.MODE_HYBRID, _prefill(512, 0), _decode([16384] * 64))
-        assert st["decode_first"] == 0
+        assert st["fixed_order"] == 0
+    # a small batch resident in one round: prefill tasks to the first workgroup ids
+    spec = inputs.CONFIGS[2]
+    st = plan(_cfg(2), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
+              _decode(inputs.draw_context_lens(2, 0)))
+    assert st["grid"] <= 512 and st["cu_prefill_x256"] > 0 and st["fixed_order"] == 1
+    # the long-context batch takes several rounds: claims
+    spec = inputs.CONFIGS[3]
+    st = plan(_cfg(3), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
+              _decode(inputs.draw_context_lens(3, 0)))
+    assert st["grid"] > 512 and st["fixed_order"] == 0
 
 
 @pytest.mark.parametrize("bad,code", [

@@ -156,7 +156,7 @@ def test_decode_first_by_workgroup_id():
         op, od = run.hybrid()
         st = run.att.stats()
         say(f"decode first plan {st}")
-        assert st["decode_first"] == 1 and st["cu_prefill_x256"] == 0
+        assert st["fixed_order"] == 2 and st["cu_prefill_x256"] == 0
         check_against_oracle(run, op, od, label="decode first")
         sp_, sd_ = run.separate()
         assert torch.equal(op, sp_) and torch.equal(od, sd_)
@@ -168,11 +168,13 @@ def test_decode_first_by_workgroup_id():
 def test_fused_launch_in_a_captured_graph(persistent):
     # the control words are restored by the launch itself, so replays of a
     # captured launch (with eager work in between) give the eager result every time
-    run = Run(inputs.make_batch(SMALL[4], seed=12), persistent=persistent)
+    # 256-token decode splits make the grid longer than one round, so roles are claimed
+    sp = spec("bf16", 8, 2, 128, 64, 12000, [8192] * 40)
+    run = Run(inputs.make_batch(sp, seed=12), persistent=persistent, decode_split_tokens=256)
     try:
         ref = run.hybrid()
         st = run.att.stats()
-        assert st["decode_first"] == 0 and st["policy"] == pod.POD_POLICY_CU_BALANCED  # roles are claimed
+        assert st["fixed_order"] == 0 and st["policy"] == pod.POD_POLICY_CU_BALANCED  # roles are claimed
         assert st["persistent"] == persistent
         op, od = run.outputs()
         side = torch.cuda.Stream()
