@@ -208,12 +208,13 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   // (prefill: its FLOPs at the tile's rate, or one task's duration if the
   // chunk has few tasks):
   //  * prefill longer: prefill takes every slot and decode fills its tail;
-  //  * prefill under 2/7 of decode: decode first, prefill fills the tail.
+  //  * prefill under 4/11 of decode: decode first, prefill fills the tail.
   //    Decode streams KV at ~83% of the HBM peak on its own, so a short
   //    prefill has little to hide behind; sharing the CUs with it slowed
   //    the decode by more than the prefill took alone (measured on every
-  //    512-token chunk of a 16K prompt beside 64 16K decodes, and on
-  //    1024-token chunks up to offset 8K);
+  //    512-token chunk of a 16K prompt beside 64 16K decodes, on
+  //    1024-token chunks up to offset 11K and 2048-token chunks up to 4K;
+  //    from 12K and 6K on, the overlap below won);
   //  * otherwise, a large batch: the roles overlap on every CU (the
   //    method's premise) with 1.5 prefill slots per CU on average -- a
   //    decode workgroup beside a prefill one streams at close to its full
@@ -236,7 +237,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
       pl.cu_prefill_x256 = lim.slots_x256;
     else if (t_p >= t_d)
       pl.cu_prefill_x256 = 256 * lim.wg_per_cu;
-    else if (3.5 * t_p < t_d)
+    else if (2.75 * t_p < t_d)
       pl.cu_prefill_x256 = 0;
     else if (t_d >= kOverlapMinSeconds)
       pl.cu_prefill_x256 = 384;

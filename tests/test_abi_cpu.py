@@ -162,11 +162,18 @@ def test_fixed_order_only_for_one_round():
     for kw in (dict(persistent=1), dict(policy=pod.POD_POLICY_PROPORTIONAL)):
         st = plan(_cfg(3, **kw), pod.MODE_HYBRID, _prefill(512, 0), _decode([16384] * 64))
         assert st["fixed_order"] == 0
-    # a small batch resident in one round: prefill tasks to the first workgroup ids
+    # small batches resident in one round: roles to workgroup ids, decode
+    # first when the prefill is under 4/11 of the decode, else prefill first
     spec = inputs.CONFIGS[2]
     st = plan(_cfg(2), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
               _decode(inputs.draw_context_lens(2, 0)))
+    assert st["grid"] <= 512 and st["cu_prefill_x256"] == 0 and st["fixed_order"] == 2
+    spec = inputs.CONFIGS[1]
+    st = plan(_cfg(1), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
+              _decode(inputs.draw_context_lens(1, 0)))
     assert st["grid"] <= 512 and st["cu_prefill_x256"] > 0 and st["fixed_order"] == 1
+    st = plan(_cfg(3), pod.MODE_HYBRID, _prefill(256, 2048), _decode([4000] * 16))
+    assert st["grid"] <= 512 and 0 < st["cu_prefill_x256"] < 512 and st["fixed_order"] == 1
     # the long-context batch takes several rounds: claims
     spec = inputs.CONFIGS[3]
     st = plan(_cfg(3), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
