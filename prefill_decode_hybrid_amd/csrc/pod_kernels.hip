@@ -1127,8 +1127,17 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
     // page id of the next block to issue, read one step ahead of its use
     int pid_next = pids[prefill_wave_page_index<D>(kb_of(C::NS - 1), t.Lp, pg0)];
     // per-lane LDS byte offsets of the MFMA operands inside a stage
-    const int krow_off = rl * C::ROWB;
-    const int ksw = ksw_rows<C::CH>(rl);
+    // Per-lane byte offsets of the K operand reads inside a stage.  The mask
+    // (a no-op: they are below one stage) tells the compiler they are
+    // non-negative, so the stage base folds into the LDS read's immediate
+    // offset instead of costing an add per read.
+    uint32_t koff[KS];
+    {
+      const int ksw = ksw_rows<C::CH>(rl);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        koff[ks] = (uint32_t)(rl * C::ROWB + (((2 * ks + half) ^ ksw) << 4)) & 0xffffu;
+    }
     const int gq = lane >> 4, ti = lane & 15;
     const int th = gq >> 1, tdh = gq & 1, tk = ti >> 2, tj = ti & 3;
     const float c2 = p.scale_log2;
@@ -1140,7 +1149,7 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
       for (int j = 0; j < 16; ++j) s[j] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + krow_off + (((2 * ks + half) ^ ksw) << 4));
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + koff[ks]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
       }
       return s;
