@@ -1169,9 +1169,12 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
       float mx = sc[0];
 #pragma unroll
       for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[j]);
-      mx = fmaxf(mx, xor_lane(mx, 32)) * c2;  // scale > 0: the max commutes with it
+      mx *= c2;  // this lane's half of the row; scale > 0: the max commutes with it
+      // A row's maximum exceeds m + 8 only if one of its two halves does, so
+      // the halves (lanes l and l ^ 32) are combined on the rare rescale path
+      // only, keeping the cross-lane exchange off every block's critical path.
       if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
-        const float mnew = fmaxf(m, mx);
+        const float mnew = fmaxf(m, fmaxf(mx, xor_lane(mx, 32)));
         const float alpha = fast_exp2(m - safe_max(mnew));
         l *= alpha;
 #pragma unroll
