@@ -17,7 +17,7 @@ SOURCES = ["pod_kernels.hip", "pod_attn.cpp", "pod_plan.cpp"]
 ARCH = os.environ.get("POD_ATTN_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
-HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fno-honor-nans", f"--offload-arch={ARCH}",
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
 
