@@ -63,6 +63,47 @@ def kernel_code_hash(lib: str = os.path.join(HERE, "libpodattn.so")):
     return None if code is None else hashlib.sha256(code).hexdigest()[:16]
 
 
+def kernel_resources(lib: str = os.path.join(HERE, "libpodattn.so")) -> dict:
+    """Per-kernel resources of the library's gfx950 code object, read from its
+    AMDGPU metadata note: {kernel name: {"vgpr", "agpr", "sgpr", "lds",
+    "scratch"}} (registers per lane, bytes of static LDS and of private
+    memory per work-item)."""
+    import msgpack
+    fat = _elf_section(lib, ".hip_fatbin")
+    if fat is None or not fat.startswith(b"__CLANG_OFFLOAD_BUNDLE__"):
+        raise ValueError(f"{lib}: no uncompressed offload bundle")
+    n, = struct.unpack_from("<Q", fat, 24)
+    pos, code = 32, None
+    for _ in range(n):
+        off, size, tlen = struct.unpack_from("<QQQ", fat, pos)
+        triple = fat[pos + 24: pos + 24 + tlen].decode()
+        pos += 24 + tlen
+        if triple.endswith("gfx950"):
+            code = fat[off: off + size]
+    if code is None:
+        raise ValueError(f"{lib}: no gfx950 code object")
+    shoff, = struct.unpack_from("<Q", code, 0x28)
+    shentsize, shnum = struct.unpack_from("<HH", code, 0x3A)
+    out = {}
+    for k in range(shnum):
+        _, typ, _, _, off, size = struct.unpack_from("<IIQQQQ", code, shoff + k * shentsize)
+        if typ != 7:  # SHT_NOTE
+            continue
+        p = off
+        while p < off + size:
+            namesz, descsz, ntype = struct.unpack_from("<III", code, p)
+            p += 12 + ((namesz + 3) & ~3)
+            desc = code[p: p + descsz]
+            p += (descsz + 3) & ~3
+            if ntype != 32:  # NT_AMDGPU_METADATA
+                continue
+            for kern in msgpack.unpackb(desc, raw=False)["amdhsa.kernels"]:
+                out[kern[".name"]] = dict(vgpr=kern[".vgpr_count"], agpr=kern.get(".agpr_count", 0),
+                                          sgpr=kern[".sgpr_count"], lds=kern[".group_segment_fixed_size"],
+                                          scratch=kern[".private_segment_fixed_size"])
+    return out
+
+
 def short_name(name: str) -> str:
     n = name.replace("void ", "").split("(")[0]
     return n.replace("pod::", "")
