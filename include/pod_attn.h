@@ -188,6 +188,9 @@ typedef struct {
     int32_t fixed_order;        /* fused launch: 0 roles claimed after dispatch; 1 / 2
                                    the prefill / decode tasks went to the first
                                    workgroup ids (a launch resident in one round)     */
+    int32_t prefill_priority;   /* 1: prefill waves issued above co-resident decode
+                                   waves; 0: equal (a decode-first launch whose
+                                   workgroups all start in the first round)         */
 } pod_attn_stats;
 
 /* Validate `cfg`, pick the device, reserve the workspace.  Returns POD_OK and

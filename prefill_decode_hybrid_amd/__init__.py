@@ -66,7 +66,7 @@ class PodAttnStats(ctypes.Structure):
         "prefill_heads_per_tile", "prefill_tiles", "prefill_splits", "prefill_split_keys",
         "prefill_tasks", "decode_split_tokens", "decode_wave_tasks", "decode_wg_tasks",
         "share_num", "share_den", "cu_prefill_x256", "policy", "prefill_chunks", "persistent",
-        "fixed_order")]
+        "fixed_order", "prefill_priority")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

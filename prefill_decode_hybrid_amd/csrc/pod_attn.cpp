@@ -80,6 +80,7 @@ void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
   st->prefill_chunks = pl.has_p ? pl.n_chunks : 0;
   st->persistent = pl.persistent ? 1 : 0;
   st->fixed_order = pl.fixed_order;
+  st->prefill_priority = pl.prefill_priority;
   st->prefill_splits = pl.has_p ? pl.ch[0].splits : 0;
   st->prefill_split_keys = pl.has_p ? pl.ch[0].split_keys : 0;
   st->prefill_tasks = pl.has_p ? pl.p_tasks : 0;
@@ -210,6 +211,7 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
   p.cu_prefill_x256 = pl.cu_prefill_x256;
   p.policy = pl.policy;
   p.fixed_order = pl.fixed_order;
+  p.prefill_priority = pl.prefill_priority;
   p.grid = pl.grid;
 
   int which = pod::kKernelHybrid;

@@ -1413,12 +1413,12 @@ struct PfSel;
 template <int D>
 struct PfSel<Bf16, D> {
   static constexpr int STAGE = PfBf16<D>::STAGE;
-  // Where a prefill tile shares a SIMD with decode waves, it issues first:
-  // its matrix and vector work is the longer pole, while a decode wave
-  // mostly waits on memory (measured: ~1% faster on the long-context batch;
-  // the opposite order made it ~13% slower).
+  // Where a prefill tile shares a SIMD with decode waves, it issues first
+  // unless the plan says otherwise: its matrix and vector work is the longer
+  // pole, while a decode wave mostly waits on memory (measured: ~1% faster
+  // on the long-context batch; the opposite order made it ~13% slower).
   static DEV void run(const PodParams& p, int task, const LdsBufs& lb) {
-    __builtin_amdgcn_s_setprio(1);
+    if (p.prefill_priority) __builtin_amdgcn_s_setprio(1);
     prefill_tile_bf16<D>(p, task, lb);
     __builtin_amdgcn_s_setprio(0);
   }

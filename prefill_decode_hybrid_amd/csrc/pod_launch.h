@@ -52,6 +52,7 @@ struct PodParams {
   uint32_t* tickets;  // per-CU words: ticket counters, or running prefill | decode << 16
   int share_num, share_den, cu_prefill_x256, policy, grid;
   int fixed_order;   // fused launch: 1 / 2 = the first workgroup ids run the prefill / decode tasks
+  int prefill_priority;  // 1: prefill waves issue above decode waves (s_setprio)
 };
 
 // The parameter block is the kernels' only argument (kernel arguments are

@@ -288,6 +288,14 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     else if (pl.grid <= slots)
       pl.fixed_order = 1;
   }
+  // Prefill waves issue above co-resident decode waves where the prefill is
+  // the longer role or runs in the decode's tail.  When a decode-first
+  // launch starts every workgroup in the first round, the decode is the
+  // critical path from the start, and the roles issue at equal priority
+  // (measured: the small Llama-3-8B batch 81.5 -> 77.5 us; decode-first
+  // chunks of a 16K prompt beside 64 16K decodes, whose prefill runs in the
+  // decode's tail, lost 4-6% at equal priority).
+  if (pl.fixed_order == 2 && pl.grid <= slots) pl.prefill_priority = 0;
   if (pl.has_p && pl.has_d && lim.persistent) {
     pl.persistent = true;  // every resident slot loops over the queues
     pl.grid = (int)std::min<int64_t>(pl.grid, slots);

@@ -115,6 +115,7 @@ struct Plan {
   int share_num = 0, share_den = 1, cu_prefill_x256 = 0, policy = 0;
   bool persistent = false;  // the fused launch is a resident grid of workgroups
   int fixed_order = 0;  // 0: roles claimed; 1 / 2: prefill / decode tasks by workgroup id first (no claims)
+  int prefill_priority = 1;  // issue priority of prefill waves beside decode waves (0 or 1)
 };
 
 // Rows of one wave's query block and keys per staged KV block, per dtype.

@@ -181,6 +181,25 @@ def test_fixed_order_only_for_one_round():
     assert st["grid"] > 512 and st["fixed_order"] == 0
 
 
+def test_prefill_priority_rule():
+    # equal issue priority only for a decode-first launch whose workgroups all
+    # start in the first round (the decode is the critical path from the start)
+    spec = inputs.CONFIGS[2]
+    st = plan(_cfg(2), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
+              _decode(inputs.draw_context_lens(2, 0)))
+    assert st["fixed_order"] == 2 and st["grid"] <= 512 and st["prefill_priority"] == 0
+    # decode first, prefill in the decode's tail (grid above one round)
+    st = plan(_cfg(3), pod.MODE_HYBRID, _prefill(512, 8192), _decode([16384] * 64))
+    assert st["fixed_order"] == 2 and st["grid"] > 512 and st["prefill_priority"] == 1
+    for cid in (1, 3, 4, 5):
+        spec = inputs.CONFIGS[cid]
+        st = plan(_cfg(cid), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
+                  _decode(inputs.draw_context_lens(cid, 0)))
+        assert st["prefill_priority"] == 1, cid
+    st = plan(_cfg(2), pod.MODE_PREFILL, _prefill(512, 0), None)
+    assert st["prefill_priority"] == 1
+
+
 @pytest.mark.parametrize("bad,code", [
     (dict(prefill=(0, 0)), pod.POD_ERR_INVALID_ARG),       # empty chunk
     (dict(prefill=(8, -1)), pod.POD_ERR_INVALID_ARG),      # negative offset
