@@ -1126,7 +1126,6 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
                              t.Lp, kb_of(s), dma, lb.st[s]);
     // page id of the next block to issue, read one step ahead of its use
     int pid_next = pids[prefill_wave_page_index<D>(kb_of(C::NS - 1), t.Lp, pg0)];
-    // per-lane LDS byte offsets of the MFMA operands inside a stage
     // Per-lane byte offsets of the K operand reads inside a stage.  The mask
     // (a no-op: they are below one stage) tells the compiler they are
     // non-negative, so the stage base folds into the LDS read's immediate
