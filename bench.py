@@ -172,7 +172,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this hot path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(sharding is described in DESIGN.md, not built)", file=sys.stderr)
+              "(the path would shard by kv-head group; that is not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -12,7 +12,7 @@ paper builds on) and heads are grouped (GQA, same list). Llama-3-8B shapes
 (32 query / 8 KV heads, head dim 128) come from the models named in the
 artifact checklist (§A.2) and the split-limiting study (§5.4.3, Table 8).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * K = 1024 tokens ("16K" = 16384).
   * Softmax scale = 1/sqrt(d).
   * A request's own K/V (including the prefill chunk's and each decode's
