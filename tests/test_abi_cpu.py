@@ -141,7 +141,7 @@ def test_decode_split_is_the_same_in_every_mode():
     assert a["decode_wave_tasks"] == b["decode_wave_tasks"]
 
 
-@pytest.mark.parametrize("P0,x", [(0, 0), (4096, 0), (15872, 0), (15360, 384)])
+@pytest.mark.parametrize("P0,x", [(0, 0), (4096, 0), (15872, 0), (15360, 352)])
 def test_role_mix_by_work_ratio(P0, x):
     # 64 decodes of 16K beside one chunk of a 16K prompt: a short chunk runs
     # after the decodes, a long one overlaps them on every CU
