@@ -24,6 +24,7 @@
 #include <cstdint>
 
 #include "pod_launch.h"
+#include "pod_units.h"
 
 namespace pod {
 
@@ -310,44 +311,40 @@ struct DecFrag {
   static constexpr int DW = EPL * E::bytes / 4;
 };
 
-// Decode units are numbered longest first: the full T-token splits of every
-// request (request by request), then each request's shorter remainder split
-// (L mod T tokens, if any), so the last tasks to be claimed are the short
-// ones.  Find (request r, split s, splits S of r, base = units of the
-// requests before r in request order) of `unit` by a wave-wide scan of the
-// per-request counts; `base + s` indexes the request's partial records.
+// Find (request r, split s, splits S of r, base = splits of the requests
+// before r) of decode unit `unit` (numbering and packing: pod_units.h) by a
+// wave-wide prefix scan of the packed per-request counts, 64 requests at a
+// time; `base + s` indexes the request's partial records.  Context lengths
+// are clamped to the batch's largest host length, so a request never has
+// more splits than the plan allowed for, and a unit whose records would
+// fall outside the plan's (possible only if the device lengths differ from
+// the host copy the launch was planned from) is dropped instead of written.
 DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S, int& base) {
   const int lane = lane_id();
-  const int maxlen = p.stride * kPageSize;
   const bool rem = unit >= p.d_full;
-  const int u = rem ? unit - p.d_full : unit;
-  int key_acc = 0, base_acc = 0;
-  for (int c0 = 0; c0 < p.N; c0 += 64) {
+  const uint32_t u = (uint32_t)(rem ? unit - p.d_full : unit);
+  uint32_t key_acc = 0, base_acc = 0;
+  for (int c0 = 0; c0 < p.N; c0 += kUnitScanLanes) {
     const int idx = c0 + lane;
-    int L = idx < p.N ? min(p.ctx[idx], maxlen) : 0;
+    int L = idx < p.N ? min(p.ctx[idx], p.ctx_cap) : 0;
     L = max(L, 0);
-    const int full = L / p.T, part = L % p.T ? 1 : 0;
-    // (units of the request) << 16 | (units of this phase); both < 2^16 per 64 requests
-    const int own = ((full + part) << 16) | (rem ? part : full);
-    int incl = own;
+    const uint32_t own = unit_pack(L, p.T, rem);
+    uint32_t incl = own;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      int v = __shfl_up(incl, off, 64);
+      const uint32_t v = __shfl_up(incl, off, 64);
       if (lane >= off) incl += v;
     }
-    const int total = __shfl(incl, 63, 64);
-    if (u < key_acc + (total & 0xffff)) {
-      const uint64_t hit = __ballot(key_acc + (incl & 0xffff) > u);
+    const uint32_t total = __shfl(incl, 63, 64);
+    if (u < key_acc + unit_phase(total)) {
+      const uint64_t hit = __ballot(key_acc + unit_phase(incl) > u);
       const int first = __builtin_ctzll(hit);
-      const int f_incl = __shfl(incl, first, 64), f_own = __shfl(own, first, 64);
       r = c0 + first;
-      S = f_own >> 16;
-      s = rem ? S - 1 : u - key_acc - ((f_incl & 0xffff) - (f_own & 0xffff));
-      base = base_acc + (f_incl >> 16) - S;
-      return true;
+      unit_select(u, rem, key_acc, base_acc, __shfl(own, first, 64), __shfl(incl, first, 64), s, S, base);
+      return base >= 0 && base + S <= p.d_units;
     }
-    key_acc += total & 0xffff;
-    base_acc += total >> 16;
+    key_acc += unit_phase(total);
+    base_acc += unit_total(total);
   }
   return false;
 }
@@ -396,7 +393,7 @@ DEV void decode_wave(const PodParams& p, int wt, float* wl) {
   s = __builtin_amdgcn_readfirstlane(s);
   S = __builtin_amdgcn_readfirstlane(S);
   base = __builtin_amdgcn_readfirstlane(base);
-  const int L = min(p.ctx[r], p.stride * kPageSize);
+  const int L = min(p.ctx[r], p.ctx_cap);
   const int t0 = s * p.T;
   const int t1 = min(t0 + p.T, L);
   const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
@@ -629,7 +626,7 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   s = __builtin_amdgcn_readfirstlane(s);
   S = __builtin_amdgcn_readfirstlane(S);
   base = __builtin_amdgcn_readfirstlane(base);
-  const int L = min(p.ctx[r], p.stride * kPageSize);
+  const int L = min(p.ctx[r], p.ctx_cap);
   const int t0 = s * p.T;
   const int t1 = min(t0 + p.T, L);
   const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
@@ -1565,11 +1562,25 @@ DEV void pick_and_claim(const PodParams& p, int& role, int& task, bool& counted,
 // complete (vmcnt 0) before the count, so the clear lands after all of them
 // without cache maintenance (an acquire-release count here, which writes
 // back and invalidates the L2, made the fused launch 3-7% slower).
-DEV void leave_claims(const PodParams& p) {
+// Returns true for that last workgroup.
+DEV bool leave_claims(const PodParams& p) {
   wait_vmem();
   const uint32_t n = __hip_atomic_fetch_add(p.ctrl + kCtrlExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (n == (uint32_t)p.grid - 1u)
-    for (int q = 0; q < kCtrlUsed; ++q) __hip_atomic_store(p.ctrl + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (n != (uint32_t)p.grid - 1u) return false;
+  for (int q = 0; q < kCtrlUsed; ++q) __hip_atomic_store(p.ctrl + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// Under the ticket policies the per-CU words count arrivals and are never
+// counted down by their workgroups; the last workgroup out of a launch (all
+// claims are done by then) clears them with all its threads, so the next
+// launch starts its ticket sequences at zero like the first one did.
+DEV void clear_tickets(const PodParams& p) {
+  for (int i = threadIdx.x; i < kTicketSlots; i += blockDim.x)
+    __hip_atomic_store(p.tickets + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV bool ticket_policy(const PodParams& p) {
+  return p.policy == kPolicyProportional || p.policy == kPolicyHalf;
 }
 
 // Fused hybrid kernel.  A regular grid of prefill tasks + decode workgroup
@@ -1594,11 +1605,11 @@ DEV void leave_claims(const PodParams& p) {
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   POD_DECLARE_LDS(E, D);
-  __shared__ int role_task[3];
+  __shared__ int role_task[4];
   __shared__ uint32_t cu_word;
   if (threadIdx.x == 0) {
     int role, task = 0;
-    bool counted = false;
+    bool counted = false, last = false;
     uint32_t key = 0;
     if (p.policy == kPolicyStatic) {
       role = (int)blockIdx.x < p.p_tasks ? 0 : 1;
@@ -1610,15 +1621,17 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
       task = role == first ? (int)blockIdx.x : (int)blockIdx.x - n_first;
     } else {
       pick_and_claim(p, role, task, counted, key);
-      leave_claims(p);  // one claim per workgroup
+      last = leave_claims(p);  // one claim per workgroup
     }
     cu_word = key;
     role_task[0] = role;
     role_task[1] = task;
     role_task[2] = counted;
+    role_task[3] = last;
   }
   __syncthreads();
   const int role = role_task[0], task = role_task[1];
+  if (role_task[3] && ticket_policy(p)) clear_tickets(p);
   if (role == 0) {
     if (task < p.p_tasks) PfSel<E, D>::run(p, task, lb);
   } else {
@@ -1637,22 +1650,24 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
 template <class E, int D, int G>
 __global__ __launch_bounds__(256, 2) void pod_persistent_kernel(PodParams p) {
   POD_DECLARE_LDS(E, D);
-  __shared__ int role_task[3];
+  __shared__ int role_task[4];
   __shared__ uint32_t cu_word;
   while (true) {
     if (threadIdx.x == 0) {
       int role, task = 0;
-      bool counted;
+      bool counted, last = false;
       uint32_t key;
       pick_and_claim(p, role, task, counted, key);
-      if (task >= (role == 0 ? p.p_tasks : p.d_wg_tasks)) leave_claims(p);  // both queues empty
+      if (task >= (role == 0 ? p.p_tasks : p.d_wg_tasks)) last = leave_claims(p);  // both queues empty
       cu_word = key;
       role_task[0] = role;
       role_task[1] = task;
       role_task[2] = counted;
+      role_task[3] = last;
     }
     __syncthreads();
     const int role = role_task[0], task = role_task[1];
+    if (role_task[3] && ticket_policy(p)) clear_tickets(p);
     if (role == 0) {
       if (task >= p.p_tasks) break;  // both queues empty (uniform: read from LDS)
       PfSel<E, D>::run(p, task, lb);

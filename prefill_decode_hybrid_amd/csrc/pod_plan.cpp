@@ -188,17 +188,20 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   if (pl.has_d) {
     if (d.N < 1 || d.N > lim.max_num_decode || d.stride < 1 || !d.ctx_host) return POD_ERR_INVALID_ARG;
     int64_t total = 0;
+    int longest = 0;
     for (int r = 0; r < d.N; ++r) {
       int L = d.ctx_host[r];
       if (L < 1 || L > lim.max_context || (int64_t)L > (int64_t)d.stride * kPageSize)
         return POD_ERR_INVALID_ARG;
       total += L;
+      longest = std::max(longest, L);
     }
     int64_t cap_total = lim.max_total_context > 0 ? lim.max_total_context
                                                   : (int64_t)lim.max_num_decode * lim.max_context;
     if (total > cap_total) return POD_ERR_INVALID_ARG;
     pl.N = d.N;
     pl.d_total = total;
+    pl.d_max = longest;
   }
 
   // Prefill workgroups kept running per CU (CU-balanced policy), in 1/256
@@ -264,6 +267,8 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     T = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(min_split_tokens(s.dtype, lim.max_context), T));
     if (lim.split_tokens > 0) T = lim.split_tokens;
     pl.T = (int)T;
+    // the kernels' unit scan holds at most kMaxSplitsPerRequest splits per request
+    if (ceil_div(pl.d_max, T) > kMaxSplitsPerRequest) return POD_ERR_UNSUPPORTED;
     int64_t units = 0, full = 0;
     for (int r = 0; r < d.N; ++r) {
       units += ceil_div(d.ctx_host[r], T);

@@ -17,6 +17,8 @@
 
 #include <cstdint>
 
+#include "pod_units.h"
+
 namespace pod {
 
 enum { kBf16 = 0, kF32 = 1 };
@@ -29,7 +31,7 @@ constexpr int kSplitIdRegs = 4;         // page-id registers of a decode wave (6
 constexpr int kMaxSplitTokens = 64 * kPageSize * kSplitIdRegs;  // 4096 tokens per decode wave task
 constexpr int kMinSplitTokens = 256;
 constexpr int kMinSplitTokensF32 = 64;  // the fp32 decode wave is latency-bound: shorter splits
-constexpr int kMaxSplitsPerRequest = 1023;  // the unit scan packs split counts in 10 bits
+constexpr int kMaxSplitsPerRequest = kUnitMaxSplits;  // 64 requests' split counts share 16 bits of the unit scan
 constexpr int kMaxContext = kMaxSplitsPerRequest * kMinSplitTokens;  // 261888 tokens
 
 // Shortest decode split for `dtype` that keeps every context up to
@@ -109,6 +111,7 @@ struct Plan {
   // decode
   bool has_d = false;
   int N = 0, T = 0, d_wave_tasks = 0, d_wg_tasks = 0;
+  int d_max = 0;        // longest decode context
   int64_t d_total = 0;  // sum of decode contexts
   int d_full = 0;       // decode units that are full T-token splits
   // fused scheduling
