@@ -60,23 +60,41 @@ def errors(got, ref):
     return float(np.max(d)) if d.size else 0.0, float(np.mean(d)) if d.size else 0.0, bool(np.isfinite(g).all())
 
 
-def check_against_oracle(run: Run, op, od, rows=None, reqs=None, label=""):
+def _oracle_errors(got, ref_fn, idx, step, label, what):
+    """Max and mean |got - oracle| over the rows idx (all rows if None),
+    computing the oracle `step` rows at a time with a progress line each."""
+    n = got.shape[0] if idx is None else len(idx)
+    picks = list(range(got.shape[0])) if idx is None else list(idx)
+    mx, tot, cnt, fin = 0.0, 0.0, 0, True
+    for a in range(0, n, step):
+        part = picks[a:a + step]
+        ref = ref_fn(part)
+        g = got[torch.as_tensor(part, device=got.device)]
+        m, mean, f = errors(g, ref)
+        mx, tot, cnt, fin = max(mx, m), tot + mean * ref.size, cnt + ref.size, fin and f
+        if n > step:
+            say(f"    {label} {what}: rows {a + len(part)}/{n} max so far {mx:.2e}")
+    return mx, (tot / cnt if cnt else 0.0), fin
+
+
+def check_against_oracle(run: Run, op, od, rows=None, reqs=None, label="", step=None):
+    """Compare the outputs with the fp64 oracle on rows / reqs (all if None).
+    step: compute the oracle that many rows (requests) at a time, printing
+    progress (for batches whose oracle takes minutes)."""
     b = run.cpu
     tol = TOL[b.spec["dtype"]]
     report = {}
     if op is not None:
-        ref = oracle.prefill(b.q_prefill, b.k_pool, b.v_pool, b.page_table_prefill, b.chunk_offset,
-                             b.sm_scale, rows=rows)
-        got = op if rows is None else op[torch.as_tensor(rows, device=op.device)]
-        mx, mn, fin = errors(got, ref)
+        ref_fn = lambda part: oracle.prefill(b.q_prefill, b.k_pool, b.v_pool, b.page_table_prefill,
+                                             b.chunk_offset, b.sm_scale, rows=part)
+        mx, mn, fin = _oracle_errors(op, ref_fn, rows, step or op.shape[0], label, "prefill")
         report["prefill"] = (mx, mn)
         assert fin, f"{label}: non-finite prefill output"
         assert mx <= tol["max"] and mn <= tol["mean"], f"{label}: prefill max {mx:.3e} mean {mn:.3e}"
     if od is not None:
-        ref = oracle.decode(b.q_decode, b.k_pool, b.v_pool, b.page_table_decode, b.context_lens,
-                            b.sm_scale, reqs=reqs)
-        got = od if reqs is None else od[torch.as_tensor(reqs, device=od.device)]
-        mx, mn, fin = errors(got, ref)
+        ref_fn = lambda part: oracle.decode(b.q_decode, b.k_pool, b.v_pool, b.page_table_decode,
+                                            b.context_lens, b.sm_scale, reqs=part)
+        mx, mn, fin = _oracle_errors(od, ref_fn, reqs, step or od.shape[0], label, "decode")
         report["decode"] = (mx, mn)
         assert fin, f"{label}: non-finite decode output"
         assert mx <= tol["max"] and mn <= tol["mean"], f"{label}: decode max {mx:.3e} mean {mn:.3e}"

@@ -42,6 +42,17 @@ def test_two_workgroups_fit_one_cu(res):
 def test_launched_kernels_use_no_scratch(res):
     # the optional persistent grid (bf16 d=128, G=8; fp32) keeps a few bytes
     for name, r in res.items():
-        kind = _short(name)[0]
-        if kind != "pod_persistent_kernel":
+        short = _short(name)
+        if short is None:  # the fill kernel of the allocation-free entry point
+            assert "pod_zero_kernel" in name, name
+        if short is None or short[0] != "pod_persistent_kernel":
             assert r["scratch"] == 0, (name, r)
+
+
+def test_gpu_parity_cases_reach_every_instantiation(res):
+    # every (dtype, head dim, group size) the library builds appears in a
+    # small GPU parity case checked against the oracle
+    from parity_cases import SMALL, instantiation
+    built = {(t[1], int(t[2]), int(t[3])) for t in (_short(n) for n in res) if t}
+    covered = {({"bf16": "Bf16", "f32": "F32"}[dt], d, G) for dt, d, G in map(instantiation, SMALL)}
+    assert built == covered, f"built but not covered: {sorted(built - covered)}"
