@@ -206,6 +206,29 @@ int pod_attn_hybrid(pod_attn_handle *h, const void *k_pool, const void *v_pool, 
                     const pod_prefill_args *prefill, const pod_decode_args *decode,
                     pod_stream_t stream);
 
+/* pod_attn_hybrid without a handle, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It allocates nothing: `cfg` is validated as by
+ * pod_attn_create (its limits bound the batch the same way), the plan is
+ * made for the device named in cfg->device (-1: the current one, which the
+ * call makes current either way), and the workspace is a fixed scratch
+ * array of POD_NOALLOC_SCRATCH_BYTES in the library's device memory, one
+ * copy per GPU, reserved when the library's code is loaded on that GPU and
+ * held until the process ends.  The call enqueues two kernels on `stream`:
+ * a fill that zeroes the scratch's counters and control words (whatever an
+ * earlier call left there), then the fused launch; outputs are bit for bit
+ * those of pod_attn_hybrid on the same batch and config.  A batch whose
+ * workspace (counters, prefill-split and decode-split partials) exceeds the
+ * scratch returns POD_ERR_WORKSPACE before anything is enqueued; other
+ * errors as for pod_attn_create and pod_attn_hybrid (a HIP failure is
+ * POD_ERR_HIP; there is no handle, so no error text and no stats).  All
+ * calls on one GPU share its scratch: calls that overlap in time on one GPU
+ * (two streams, two threads) race and give undefined results. */
+#define POD_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pod_attn_hybrid_noalloc(const pod_attn_config *cfg, const void *k_pool, const void *v_pool,
+                            int64_t num_pages, const pod_prefill_args *prefill,
+                            const pod_decode_args *decode, pod_stream_t stream);
+
 /* Prefill half only (the compute-bound baseline kernel). */
 int pod_attn_prefill_only(pod_attn_handle *h, const void *k_pool, const void *v_pool,
                           int64_t num_pages, const pod_prefill_args *prefill, pod_stream_t stream);

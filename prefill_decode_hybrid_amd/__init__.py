@@ -26,7 +26,7 @@ MODE_HYBRID, MODE_PREFILL, MODE_DECODE = 0, 1, 2
 POD_MAX_CHUNKS = 64
 
 EXPORTED = ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_prefill_only",
-            "pod_attn_decode_only", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
+            "pod_attn_decode_only", "pod_attn_hybrid_noalloc", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
             "pod_attn_get_stats", "pod_attn_plan", "pod_attn_plan_varlen",
             "pod_attn_status_string", "pod_attn_last_error")
 
@@ -94,6 +94,8 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_destroy.argtypes = [P]
     lib.pod_attn_hybrid.argtypes = [P, P, P, i64, ctypes.POINTER(PodPrefillArgs),
                                     ctypes.POINTER(PodDecodeArgs), P]
+    lib.pod_attn_hybrid_noalloc.argtypes = [ctypes.POINTER(PodAttnConfig), P, P, i64, ctypes.POINTER(PodPrefillArgs),
+                                            ctypes.POINTER(PodDecodeArgs), P]
     lib.pod_attn_prefill_only.argtypes = [P, P, P, i64, ctypes.POINTER(PodPrefillArgs), P]
     lib.pod_attn_decode_only.argtypes = [P, P, P, i64, ctypes.POINTER(PodDecodeArgs), P]
     lib.pod_attn_hybrid_varlen.argtypes = [P, P, P, i64, ctypes.POINTER(PodPrefillBatch),
@@ -108,8 +110,9 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_status_string.restype = ctypes.c_char_p
     lib.pod_attn_last_error.argtypes = [P]
     lib.pod_attn_last_error.restype = ctypes.c_char_p
-    for name in ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_prefill_only",
-                 "pod_attn_decode_only", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
+    for name in ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_hybrid_noalloc",
+                 "pod_attn_prefill_only",
+                 "pod_attn_decode_only", "pod_attn_hybrid_noalloc", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
                  "pod_attn_get_stats", "pod_attn_plan", "pod_attn_plan_varlen"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -195,6 +198,16 @@ def pod_attn_hybrid(h, k_pool, v_pool, prefill: Optional[PodPrefillArgs], decode
                              ctypes.byref(prefill) if prefill is not None else None,
                              ctypes.byref(decode) if decode is not None else None, _stream_ptr(stream))
     _check(h, rc, "pod_attn_hybrid")
+
+
+def pod_attn_hybrid_noalloc(cfg: PodAttnConfig, k_pool, v_pool, prefill: Optional[PodPrefillArgs],
+                            decode: Optional[PodDecodeArgs], stream=None) -> None:
+    """pod_attn_hybrid without a handle: workspace in the library's fixed device scratch."""
+    rc = load().pod_attn_hybrid_noalloc(ctypes.byref(cfg), _ptr(k_pool), _ptr(v_pool), int(k_pool.shape[0]),
+                                        ctypes.byref(prefill) if prefill is not None else None,
+                                        ctypes.byref(decode) if decode is not None else None, _stream_ptr(stream))
+    if rc != POD_OK:
+        raise PodAttnError(rc, "pod_attn_hybrid_noalloc")
 
 
 def pod_attn_prefill_only(h, k_pool, v_pool, prefill: PodPrefillArgs, stream=None) -> None:

@@ -154,30 +154,23 @@ int check_decode(const pod_decode_args* d) {
   return POD_OK;
 }
 
-int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, int64_t num_pages,
-        const PrefillView& pv, const pod_decode_args* da, pod_stream_t stream) {
-  if (!h || !k_pool || !v_pool || num_pages < 1 || num_pages > 0xffffffffLL) return POD_ERR_INVALID_ARG;
-  int rc = check_decode(da);
-  if (rc) return rc;
-  pod::Plan pl;
-  rc = pod::make_plan(h->shape, h->lim, mode, pv.in, decode_in(da), &pl);
-  if (rc) return rc;
-
-  const pod::Shape& s = h->shape;
-  pod::PodParams p{};
+// The kernels' parameter block for plan `pl` over workspace `ws` laid out as `lay`.
+void fill_params(const pod::Shape& s, float sm_scale, char* ws, const pod::WorkspaceLayout& lay, const pod::Plan& pl,
+                 const void* k_pool, const void* v_pool, int64_t num_pages, const PrefillView& pv,
+                 const pod_decode_args* da, pod::PodParams& p) {
+  p = pod::PodParams{};
   p.k_pool = k_pool;
   p.v_pool = v_pool;
   p.num_pages = (uint32_t)num_pages;
   p.hq = s.hq;
   p.hkv = s.hkv;
-  p.scale_log2 = h->sm_scale * 1.4426950408889634f;
-  uint32_t* ctrl = reinterpret_cast<uint32_t*>(h->ws + h->lay.ctrl);
-  p.ctrl = ctrl;
-  p.tickets = reinterpret_cast<uint32_t*>(h->ws + h->lay.tickets);
-  p.p_cnt = reinterpret_cast<uint32_t*>(h->ws + h->lay.p_cnt);
-  p.d_cnt = reinterpret_cast<uint32_t*>(h->ws + h->lay.d_cnt);
-  p.p_part = reinterpret_cast<float*>(h->ws + h->lay.p_part);
-  p.d_part = reinterpret_cast<float*>(h->ws + h->lay.d_part);
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.ctrl = reinterpret_cast<uint32_t*>(ws + lay.ctrl);
+  p.tickets = reinterpret_cast<uint32_t*>(ws + lay.tickets);
+  p.p_cnt = reinterpret_cast<uint32_t*>(ws + lay.p_cnt);
+  p.d_cnt = reinterpret_cast<uint32_t*>(ws + lay.d_cnt);
+  p.p_part = reinterpret_cast<float*>(ws + lay.p_part);
+  p.d_part = reinterpret_cast<float*>(ws + lay.d_part);
   if (pl.has_p) {
     p.qp = pv.q;
     p.op = pv.o;
@@ -214,15 +207,30 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
   p.fixed_order = pl.fixed_order;
   p.prefill_priority = pl.prefill_priority;
   p.grid = pl.grid;
+}
 
-  int which = pod::kKernelHybrid;
-  if (!pl.has_d) which = pod::kKernelPrefill;
-  if (!pl.has_p) which = pod::kKernelDecode;
+int kernel_of(const pod::Plan& pl) {
+  if (!pl.has_d) return pod::kKernelPrefill;
+  if (!pl.has_p) return pod::kKernelDecode;
+  return pod::kKernelHybrid;
+}
 
+int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, int64_t num_pages,
+        const PrefillView& pv, const pod_decode_args* da, pod_stream_t stream) {
+  if (!h || !k_pool || !v_pool || num_pages < 1 || num_pages > 0xffffffffLL) return POD_ERR_INVALID_ARG;
+  int rc = check_decode(da);
+  if (rc) return rc;
+  pod::Plan pl;
+  rc = pod::make_plan(h->shape, h->lim, mode, pv.in, decode_in(da), &pl);
+  if (rc) return rc;
+
+  const pod::Shape& s = h->shape;
+  pod::PodParams p;
+  fill_params(s, h->sm_scale, h->ws, h->lay, pl, k_pool, v_pool, num_pages, pv, da, p);
   hipError_t e = hipSetDevice(h->device);
   if (e != hipSuccess) return hip_fail(h, e, "hipSetDevice");
   if (pl.grid > 0) {
-    e = (hipError_t)pod::launch(which, s.dtype, s.d, s.G, p, pl, reinterpret_cast<hipStream_t>(stream));
+    e = (hipError_t)pod::launch(kernel_of(pl), s.dtype, s.d, s.G, p, pl, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
   }
   fill_stats(pl, &h->stats);
@@ -314,6 +322,48 @@ int pod_attn_hybrid(pod_attn_handle* h, const void* k_pool, const void* v_pool, 
   PrefillView pv;
   const int rc = prefill_one(prefill, pv);
   return rc ? rc : run(h, pod::kModeHybrid, k_pool, v_pool, num_pages, pv, decode, stream);
+}
+
+int pod_attn_hybrid_noalloc(const pod_attn_config* cfg, const void* k_pool, const void* v_pool, int64_t num_pages,
+                            const pod_prefill_args* prefill, const pod_decode_args* decode, pod_stream_t stream) {
+  pod::Shape s;
+  pod::Limits lim;
+  float scale = 0.0f;
+  int rc = validate_config(cfg, s, lim, scale);
+  if (rc) return rc;
+  if (!k_pool || !v_pool || num_pages < 1 || num_pages > 0xffffffffLL) return POD_ERR_INVALID_ARG;
+  if (!pod::have_kernel(s.dtype, s.d, s.G)) return POD_ERR_UNSUPPORTED;
+  rc = check_decode(decode);
+  if (rc) return rc;
+  PrefillView pv;
+  rc = prefill_one(prefill, pv);
+  if (rc) return rc;
+
+  int dev = cfg->device;
+  hipError_t e = hipSuccess;
+  if (dev < 0) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipSetDevice(dev);
+  int cus = 0;
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus <= 0) return POD_ERR_HIP;
+  lim.num_cus = cus;
+  pod::derive_capacities(s, lim);
+  pod::Plan pl;
+  rc = pod::make_plan(s, lim, pod::kModeHybrid, pv.in, decode_in(decode), &pl);
+  if (rc) return rc;
+  // the workspace this call needs, laid out in the device's fixed scratch
+  const pod::WorkspaceLayout lay = pod::workspace_layout_for_plan(s, pl);
+  if (lay.total > pod::scratch_bytes()) return POD_ERR_WORKSPACE;
+  void* base = nullptr;
+  if (pod::scratch_address(dev, &base) != 0 || !base) return POD_ERR_HIP;
+
+  pod::PodParams p;
+  fill_params(s, scale, static_cast<char*>(base), lay, pl, k_pool, v_pool, num_pages, pv, decode, p);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // counters and control words start at zero whatever the last call left
+  if (pod::launch_zero(base, lay.p_part, st) != 0) return POD_ERR_HIP;
+  if (pl.grid > 0 && pod::launch(kernel_of(pl), s.dtype, s.d, s.G, p, pl, st) != 0) return POD_ERR_HIP;
+  return POD_OK;
 }
 
 int pod_attn_prefill_only(pod_attn_handle* h, const void* k_pool, const void* v_pool, int64_t num_pages,

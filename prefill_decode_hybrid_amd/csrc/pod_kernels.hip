@@ -22,7 +22,9 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
+#include "../../include/pod_attn.h"
 #include "pod_launch.h"
 #include "pod_units.h"
 
@@ -1721,6 +1723,51 @@ int launch(int which, int dtype, int d, int G, const PodParams& p, const Plan& p
   POD_KERNEL_LIST(POD_DISPATCH)
 #undef POD_DISPATCH
   return (int)hipErrorInvalidValue;
+}
+
+// ------------------------------------------------- allocation-free scratch
+// Workspace of pod_attn_hybrid_noalloc: a fixed array in the code object's
+// device memory, one copy per GPU the library runs on, held until the
+// process ends.  Calls on one GPU share it (and race if they overlap).
+constexpr size_t kScratchBytes = POD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+size_t scratch_bytes() { return kScratchBytes; }
+
+// The array's device address on `device`, looked up once per device with
+// that device current (the host-side name of the array is not a device
+// address and must never reach a kernel or a copy).
+int scratch_address(int device, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices || !out) return (int)hipErrorInvalidValue;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != device) e = hipSetDevice(device);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *out = addr[device];
+  return 0;
+}
+
+__global__ __launch_bounds__(256) void pod_zero_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+int launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const uint32_t n = (uint32_t)(bytes / 4);
+  if (n == 0) return 0;
+  const uint32_t blocks = (n + 255) / 256 < 1024u ? (n + 255) / 256 : 1024u;
+  hipLaunchKernelGGL(pod_zero_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint32_t*>(p), n);
+  return (int)hipGetLastError();
 }
 
 int have_kernel(int dtype, int d, int G) {

@@ -68,4 +68,13 @@ int launch(int which, int dtype, int d, int G, const PodParams& p, const Plan& p
 // 1 if a kernel is built for (dtype, d, G).
 int have_kernel(int dtype, int d, int G);
 
+// Fixed device scratch of the allocation-free entry point: its size, and its
+// address on `device` (looked up once per device, with that device
+// current).  0 or a hipError_t.
+size_t scratch_bytes();
+int scratch_address(int device, void** out);
+// Zero `bytes` (a multiple of 4) at `p` with a fill kernel (no memset node
+// in a captured graph).  Returns a hipError_t.
+int launch_zero(void* p, size_t bytes, hipStream_t s);
+
 }  // namespace pod

@@ -76,6 +76,17 @@ WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim) {
   return w;
 }
 
+WorkspaceLayout workspace_layout_for_plan(const Shape& s, const Plan& pl) {
+  Limits lim;
+  lim.cap_tiles = pl.has_p ? pl.tiles : 0;
+  bool split = false;
+  for (int k = 0; pl.has_p && k < pl.n_chunks; ++k) split |= pl.ch[k].splits > 1;
+  lim.cap_prefill_tasks = split ? pl.p_tasks : 0;  // partials only where tiles are split
+  lim.max_num_decode = pl.has_d ? pl.N : 0;
+  lim.cap_wave_tasks = pl.has_d ? pl.d_wave_tasks : 0;
+  return workspace_layout(s, lim);
+}
+
 static void reduce_share(int64_t a, int64_t b, int& num, int& den) {
   // prefill share a / (a + b) as num / kShareDen, at least 1 of each role
   double rho = (double)a / (double)(a + b);

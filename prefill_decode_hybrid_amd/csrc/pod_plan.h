@@ -135,6 +135,8 @@ struct WorkspaceLayout {
   size_t ctrl = 0, tickets = 0, p_cnt = 0, d_cnt = 0, p_part = 0, d_part = 0, total = 0;
 };
 WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim);
+// The workspace one planned call uses (counters and partials for exactly its tasks).
+WorkspaceLayout workspace_layout_for_plan(const Shape& s, const Plan& pl);
 
 // Validate one call and plan it.  Returns 0 or a negative pod_status.
 int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p,
