@@ -104,14 +104,29 @@ typedef struct {
     int32_t max_context;      /* largest decode context and largest offset+chunk;
                                  at most 261888 (POD_ERR_UNSUPPORTED above)            */
     int64_t max_total_context;/* largest sum of decode contexts; 0: max_num_decode*max_context */
-    int32_t wg_per_cu;        /* co-resident workgroups per CU; 0 selects 2 (only 2 built) */
-    int32_t prefill_split_cap_waves; /* cap on prefill tasks, in waves of resident
-                                 workgroups (paper §4.2.3 caps splits at two waves); 0 -> 2 */
+    int32_t wg_per_cu;        /* resource envelope: co-resident workgroups per CU.
+                                 2: <= 256 registers per lane and ~68 KB LDS per
+                                 workgroup, 32-row prefill tiles, decode by page pairs;
+                                 4 (bf16 only, not persistent): <= 128 registers and
+                                 <= 40 KB LDS, 16-row prefill tiles, decode page by
+                                 page; 0: chosen per call from its batch (paper §4.2.2
+                                 picks 2 or 4 per batch; measured here: 4 for a call
+                                 without prefill whose decode workgroups all start in
+                                 one round of 4 per CU, else 2).  With a fixed envelope
+                                 the fused call equals the split calls bit for bit;
+                                 with 0 they may pick different envelopes, whose
+                                 results differ in rounding only                      */
+    int32_t prefill_split_cap_waves; /* KV splits added to fill the machine stop at one
+                                 wave of resident workgroups and at most this many waves
+                                 (paper §4.2.3 caps splits at two waves); 0 -> 2;
+                                 -1: no cap, every tile split as finely as the minimum
+                                 split (1024 keys bf16, 32 fp32) allows              */
     int32_t policy;           /* enum pod_policy                                       */
     int32_t device;           /* HIP device ordinal; -1 selects the current device     */
     int32_t prefill_slots_x256; /* CU-balanced policy: prefill workgroups kept running per
-                                 CU, in 1/256 of a workgroup (1 .. 256 * wg_per_cu); 0
-                                 selects the planner's choice from the batch            */
+                                 CU, in 1/256 of a workgroup (1 .. 1024, at most 256 *
+                                 the envelope's workgroups per CU); 0 selects the
+                                 planner's choice from the batch                      */
     int32_t decode_split_tokens; /* tokens per decode wave task, a multiple of 16 up to
                                  4096 and at least 256 (bf16) or 64 (fp32) and
                                  max_context / 1023; 0 selects the planner's choice, which
@@ -121,6 +136,8 @@ typedef struct {
                                  wg_per_cu workgroups) that loops over the task queues
                                  until both are empty, instead of one workgroup per
                                  task; same tasks and results.  0: one per task       */
+    int32_t prefill_splits;     /* KV splits per prefill tile (at most one per minimum
+                                 split); 0 selects the planner's choice above        */
 } pod_attn_config;
 
 typedef struct {

@@ -43,11 +43,14 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   // a request has at most kMaxSplitsPerRequest decode splits of at least kMinSplitTokens
   if ((int64_t)c->max_context > (int64_t)pod::kMaxContext) return POD_ERR_UNSUPPORTED;
   if (!(c->sm_scale >= 0.0f) || !std::isfinite(c->sm_scale)) return POD_ERR_INVALID_ARG;
-  if (c->wg_per_cu != 0 && c->wg_per_cu != 2) return POD_ERR_UNSUPPORTED;
-  if (c->prefill_split_cap_waves < 0) return POD_ERR_INVALID_ARG;
-  if (c->policy < pod::kPolicyCuBalanced || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
-  if (c->prefill_slots_x256 < 0 || c->prefill_slots_x256 > 2 * 256) return POD_ERR_INVALID_ARG;
+  if (c->wg_per_cu != 0 && c->wg_per_cu != 2 && c->wg_per_cu != 4) return POD_ERR_INVALID_ARG;
   if (c->persistent != 0 && c->persistent != 1) return POD_ERR_INVALID_ARG;
+  // the four-workgroup envelope is built for bf16 and launched one workgroup per task
+  if (c->wg_per_cu == 4 && (s.dtype != pod::kBf16 || c->persistent)) return POD_ERR_UNSUPPORTED;
+  if (c->prefill_split_cap_waves < -1) return POD_ERR_INVALID_ARG;
+  if (c->prefill_splits < 0) return POD_ERR_INVALID_ARG;
+  if (c->policy < pod::kPolicyCuBalanced || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
+  if (c->prefill_slots_x256 < 0 || c->prefill_slots_x256 > 4 * 256) return POD_ERR_INVALID_ARG;
   if (c->decode_split_tokens != 0 &&
       (c->decode_split_tokens % pod::kPageSize != 0 ||
        c->decode_split_tokens < pod::min_split_tokens(s.dtype, c->max_context) ||
@@ -57,8 +60,9 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   lim.max_num_decode = c->max_num_decode;
   lim.max_context = c->max_context;
   lim.max_total_context = c->max_total_context;
-  lim.wg_per_cu = 2;
+  lim.wg_per_cu = c->persistent ? 2 : c->wg_per_cu;
   lim.cap_waves = c->prefill_split_cap_waves ? c->prefill_split_cap_waves : 2;
+  lim.prefill_splits = c->prefill_splits;
   lim.policy = c->policy;
   lim.slots_x256 = c->prefill_slots_x256;
   lim.split_tokens = c->decode_split_tokens;

@@ -82,6 +82,25 @@ DEV float row_sum16(float x) {
   return x;
 }
 DEV float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
+// Reductions over lanes l and l ^ 16 (l ^ 32) with gfx950's row-swap
+// permutes: swapping a register with itself hands every lane both values of
+// its pair, with no LDS traffic and no lane-index register.
+DEV float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+DEV float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+DEV float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+DEV float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 DEV int lane_id() { return __lane_id(); }
 DEV int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -160,6 +179,7 @@ DEV void store_out(void* base, int64_t idx, float v) {
 // with device-scope loads after its counter update has returned.  The
 // accesses go through buffer resources so that they can be 16 bytes wide.
 constexpr int kDevScope = 16;        // buffer cache-policy bit sc1 (device scope)
+constexpr int kNonTemporal = 2;      // buffer cache-policy bit nt (streamed once)
 constexpr int kMergeLdsBytes = 2048; // wave-private LDS a merge needs for its weights
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
@@ -370,14 +390,16 @@ DEV Rsrc decode_record(const PodParams& p, int unit, int g) {
 
 // Count this split's arrival at (r, g); the last of the S splits merges all
 // partials of (r, g) in split order and restores the counter to zero.
-template <class E, int D, int G>
+// IF: 16-byte partial pieces per lane loaded at once (fewer in the
+// 128-register envelope).
+template <class E, int D, int G, int IF = (E::bytes == 2 ? 16 : 4)>
 DEV void decode_finish(const PodParams& p, int r, int S, int base, int g, float* wl) {
   using Rc = DecRec<D, G>;
   uint32_t* cnt = p.d_cnt + (int64_t)r * p.hkv + g;
   if (!arrive_last(cnt, (uint32_t)S)) return;
   const char* part0 = reinterpret_cast<const char*>(p.d_part) + ((int64_t)g * p.d_units + base) * Rc::BYTES;
   char* out0 = reinterpret_cast<char*>(p.od) + ((int64_t)r * p.hq + (int64_t)g * G) * D * E::bytes;
-  merge_rows<E, G, D, (E::bytes == 2 ? 16 : 4)>(part0, Rc::BYTES, 0, Rc::M_OFF, Rc::L_OFF, S, G, out0, D, wl);
+  merge_rows<E, G, D, IF>(part0, Rc::BYTES, 0, Rc::M_OFF, Rc::L_OFF, S, G, out0, D, wl);
   if (lane_id() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -823,6 +845,214 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   decode_finish<Bf16, D, G>(p, r, S, base, g, reinterpret_cast<float*>(lds));
 }
 
+// bf16 decode wave of the four-workgroups-per-CU envelope (at most 128
+// registers per lane, 8 KB of LDS per wave): one page (16 keys) per step
+// through the wave's LDS buffer (K rows then V rows).  The next page's loads
+// are issued as soon as the current page is in LDS, so one page per wave is
+// in flight while the current one is computed, and the registers hold one
+// page of loads instead of two pairs.  QK^T on v_mfma_f32_16x16x32_bf16 as
+// in decode_wave_mfma; PV on v_mfma_f32_16x16x16_bf16 with the page's 16
+// keys as the k dimension (one transposing read per 16-wide d tile).
+template <int D>
+struct DecMfma4 {
+  static constexpr int KC = D / 32;          // QK k-chunks
+  static constexpr int DB = D / 16;          // PV d-blocks
+  static constexpr int ROWB = D * 2;         // bytes per token row of one head
+  static constexpr int CHR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CHR;       // rows per load instruction
+  static constexpr int NI = 16 / RPI;        // load instructions per page per operand
+  static constexpr int OPB = 16 * ROWB;      // LDS bytes per operand (one page)
+  static constexpr int LDS_WAVE = 2 * OPB;   // K page then V page
+  static constexpr float kLazy = 8.0f;
+};
+
+template <int D, int G>
+DEV void decode_wave_mfma4(const PodParams& p, int wt, char* lds, int* wpids) {
+  using C = DecMfma4<D>;
+  constexpr int KC = C::KC, DB = C::DB, NI = C::NI;
+  const int lane = lane_id();
+  const int hkv = p.hkv;
+  const int g = wt % hkv;
+  const int unit = wt / hkv;
+  int r, s, S, base;
+  if (!locate_unit(p, unit, r, s, S, base)) return;
+  r = __builtin_amdgcn_readfirstlane(r);
+  s = __builtin_amdgcn_readfirstlane(s);
+  S = __builtin_amdgcn_readfirstlane(S);
+  base = __builtin_amdgcn_readfirstlane(base);
+  const int L = min(p.ctx[r], p.ctx_cap);
+  const int t0 = s * p.T;
+  const int t1 = min(t0 + p.T, L);
+  const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
+  const int kk = lane & 15, q4 = lane >> 4;       // MFMA roles: key / head column, quad
+  const int lrow = lane / C::CHR, lchk = lane % C::CHR;  // load role: row in group, chunk
+
+  // page ids of the split in the wave's LDS slice (at most 256 of them):
+  // registers are too scarce in this envelope to hold them.  LDS operations
+  // of a wave run in order, so later reads see these writes.
+  const int32_t* ptr = p.pt_d + (int64_t)r * p.stride + t0 / kPageSize;
+#pragma unroll
+  for (int k = 0; k < kSplitIdRegs; ++k)
+    if (64 * k + lane < npg) wpids[64 * k + lane] = (int)min((uint32_t)ptr[64 * k + lane], p.num_pages - 1u);
+  auto page_id = [&](int i) __attribute__((always_inline)) { return wpids[min(i, npg - 1)]; };
+
+  // Q^T operand: column = head kk (< G), rows d = 32c + 8q4 .. +8
+  bf16x8_t qf[KC];
+  {
+    const char* qb = reinterpret_cast<const char*>(p.qd) +
+                     (((int64_t)r * p.hq + (int64_t)g * G + kk) * D + 8 * q4) * 2;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kk < G) v = *reinterpret_cast<const uint4*>(qb + c * 64);
+      qf[c] = as_bf16x8(v);
+    }
+  }
+  // Loads are buffer loads on a descriptor of the page (a scalar base and a
+  // 32-bit lane offset inside the page), so no 64-bit lane pointers occupy
+  // registers.
+  const uint32_t tok_bytes = (uint32_t)hkv * D * 2;
+  const uint32_t page_bytes = kPageSize * tok_bytes;
+  const uint32_t lane_off = (uint32_t)lrow * tok_bytes + (uint32_t)g * C::ROWB + lchk * 16;
+  char* kl = lds;            // K rows of the page
+  char* vl = lds + C::OPB;   // V rows of the page
+
+  f32x4_t acc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) acc[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.0f;
+
+  u32x4_t kr[NI], vr[NI];
+  auto issue = [&](int pid) __attribute__((always_inline)) {
+    const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(pid) * page_bytes;
+    const Rsrc rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(p.k_pool) + off), (short)0, (int)page_bytes, 0x00020000);
+    const Rsrc rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(p.v_pool) + off), (short)0, (int)page_bytes, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(lane_off + u * C::RPI * tok_bytes), 0, kNonTemporal);
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(lane_off + u * C::RPI * tok_bytes), 0, kNonTemporal);
+  };
+  const int tk = (lane & 15) >> 2, tj = lane & 3;
+  const int vr0 = 4 * q4 + tk;  // the key row this lane feeds to the transposing reads
+
+  issue(page_id(0));
+  int pid_next = page_id(1);
+  for (int i = 0; i < npg; ++i) {
+    const int pid_after = page_id(i + 2);  // read a page ahead of its use
+    const int kbase = t0 + kPageSize * i;
+    // page i -> LDS; LDS operations of a wave run in order, so these writes
+    // land after the previous page's reads.  Only a split's last page can
+    // hold invisible rows; their V rows are zeroed (a uniform branch, so no
+    // copies of the loaded rows are kept).
+    if (kbase + kPageSize > t1) {
+#pragma unroll
+      for (int u = 0; u < NI; ++u)
+        if (kbase + u * C::RPI + lrow >= t1) vr[u] = (u32x4_t){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int row = u * C::RPI + lrow;
+      *reinterpret_cast<u32x4_t*>(kl + row * C::ROWB + ((lchk ^ ksw_rows<C::CHR>(row)) << 4)) = kr[u];
+      *reinterpret_cast<u32x4_t*>(vl + row * C::ROWB + ((lchk ^ vsw_decode<C::CHR>(row)) << 4)) = vr[u];
+    }
+    // S^T of the page
+    f32x4_t sc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kl + kk * C::ROWB + (((4 * c + q4) ^ ksw_rows<C::CHR>(kk)) << 4));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], sc, 0, 0, 0);
+    }
+    // the next page's loads fly during the softmax and PV of this one (issued
+    // after the K reads so that both sets of operands are never live at once)
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < npg) issue(pid_next);
+    pid_next = pid_after;
+    float mloc = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = kbase + 4 * q4 + j < t1;
+      const float v = ok ? sc[j] * p.scale_log2 : kNegInf;
+      sc[j] = v;
+      mloc = fmaxf(mloc, v);
+    }
+    if (__builtin_amdgcn_ballot_w64(mloc > m + C::kLazy) != 0) {
+      const float mm = max_xor32(max_xor16(mloc));
+      const float mnew = fmaxf(m, mm);
+      const float alpha = fast_exp2(m - safe_max(mnew));
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) acc[b] *= alpha;
+      m = mnew;
+    }
+    const float mu = safe_max(m);
+    // the row sum adds the bf16 weights the PV product uses
+    uint32_t pw[2];
+    pw[0] = pack_bf16(fast_exp2(sc[0] - mu), fast_exp2(sc[1] - mu));
+    pw[1] = pack_bf16(fast_exp2(sc[2] - mu), fast_exp2(sc[3] - mu));
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[0]), kOnes2, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[1]), kOnes2, l, false);
+    const i16x4_t pf = __builtin_bit_cast(i16x4_t, make_uint2(pw[0], pw[1]));
+    // O^T += V^T P^T: lane (quad q4, 4k + j) reads key 4 q4 + k, d = 16b + 4j .. +4;
+    // four d blocks' operands in registers at a time
+#pragma unroll
+    for (int b0 = 0; b0 < DB; b0 += 4) {
+      i16x4_t va[4];
+#pragma unroll
+      for (int e = 0; e < 4 && b0 + e < DB; ++e) {
+        const int chunk = 2 * (b0 + e) + (tj >> 1);
+        va[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(
+            vl + vr0 * C::ROWB + ((chunk ^ vsw_decode<C::CHR>(vr0)) << 4) + ((tj & 1) << 3)));
+      }
+#pragma unroll
+      for (int e = 0; e < 4 && b0 + e < DB; ++e)
+        acc[b0 + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[e], pf, acc[b0 + e], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // l over the four key quads of each head column
+  l = sum_xor32(sum_xor16(l));
+  const int h = lane & 15;
+  if (S == 1) {
+    if (h < G) {
+      const float inv = 1.0f / l;
+      char* orow = reinterpret_cast<char*>(p.od) + (((int64_t)r * p.hq + (int64_t)g * G + h) * D + 4 * q4) * 2;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        uint2 w;
+        w.x = pack_bf16(acc[b][0] * inv, acc[b][1] * inv);
+        w.y = pack_bf16(acc[b][2] * inv, acc[b][3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * b) = w;
+      }
+    }
+    return;
+  }
+  using Rc = DecRec<D, G>;
+  const Rsrc rs = decode_record<D, G>(p, base + s, g);
+  if (h < G) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b) st_dev4(rs, (h * D + 16 * b + 4 * q4) * 4, acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    if (q4 == 0) {
+      st_dev1(rs, Rc::M_OFF + h * 4, m);
+      st_dev1(rs, Rc::L_OFF + h * 4, l);
+    }
+  }
+  decode_finish<Bf16, D, G, 4>(p, r, S, base, g, reinterpret_cast<float*>(lds));
+}
+
+template <int D, int G>
+DEV void decode_wg4(const PodParams& p, int wg_task, const LdsBufs& lb) {
+  const int wt = wg_task * kWavesPerWG + wave_id();
+  if (wt >= p.d_wave_tasks) return;
+  const int w = wave_id();
+  char* buf = w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3];
+  decode_wave_mfma4<D, G>(p, wt, buf, lb.pids + w * (kSplitIdRegs * 64));
+}
+
 template <class E, int D, int G, int PF>
 DEV void decode_wg(const PodParams& p, int wg_task, const LdsBufs& lb) {
   const int wt = wg_task * kWavesPerWG + wave_id();
@@ -979,7 +1209,13 @@ struct PfDma {
   uint32_t k[IPW], v[IPW];
 };
 
-template <int D>
+// V rows are swizzled for the PV operand reads of the tile that consumes
+// them: the 32-row tile reads 4 rows x 64 bytes per transposing pass
+// (vsw_prefill), the 16-row tile 8 rows x 32 bytes (vsw_decode).
+template <int CH, bool V16>
+DEV int vsw_tile(int row) { return V16 ? vsw_decode<CH>(row) : vsw_prefill<CH>(row); }
+
+template <int D, bool V16 = false>
 DEV PfDma<D> prefill_dma_offsets(int64_t tok_bytes) {
   using C = PfBf16<D>;
   const int lane = lane_id();
@@ -989,7 +1225,7 @@ DEV PfDma<D> prefill_dma_offsets(int64_t tok_bytes) {
   for (int i = 0; i < C::IPW; ++i) {
     const int row = (wave_id() * C::IPW + i) * C::RPI + lrow;
     o.k[i] = (uint32_t)((row & 15) * tok_bytes) + ((pos ^ ksw_rows<C::CH>(row)) << 4);
-    o.v[i] = (uint32_t)((row & 15) * tok_bytes) + ((pos ^ vsw_prefill<C::CH>(row)) << 4);
+    o.v[i] = (uint32_t)((row & 15) * tok_bytes) + ((pos ^ vsw_tile<C::CH, V16>(row)) << 4);
   }
   return o;
 }
@@ -1005,7 +1241,7 @@ DEV int prefill_wave_page_index(int kb0, int Lp, int pg0) {
 }
 
 // Issue the DMA loads of the block at kb0 (page id `page` for this wave).
-template <int D>
+template <int D, bool V16 = false>
 DEV void prefill_issue_block(const char* kpool, const char* vpool, int64_t tok_bytes, int page, int Lp, int kb0,
                              const PfDma<D>& off, char* stage) {
   using C = PfBf16<D>;
@@ -1029,7 +1265,7 @@ DEV void prefill_issue_block(const char* kpool, const char* vpool, int64_t tok_b
       const int row = ins * C::RPI + lrow;
       const uint32_t slot = (uint32_t)(min(kb0 + row, Lp - 1) & 15) * (uint32_t)tok_bytes;
       ko = slot + ((pos ^ ksw_rows<C::CH>(row)) << 4);
-      vo = slot + ((pos ^ vsw_prefill<C::CH>(row)) << 4);
+      vo = slot + ((pos ^ vsw_tile<C::CH, V16>(row)) << 4);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(stage + ins * 1024), 16, ko, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(stage + C::OPB + ins * 1024), 16, vo, 0, 0, 0);
@@ -1065,7 +1301,7 @@ DEV void prefill_finish_split(const PodParams& p, const TaskGeom& t, int task, c
   const char* part0 = reinterpret_cast<const char*>(p.p_part) + (int64_t)(task - t.split * t.tiles) * Rc::BYTES;
   char* out0 = reinterpret_cast<char*>(p.op) + ((int64_t)(t.row_base + t.row0) * p.hq + t.head) * D * E::bytes;
   float* wl = reinterpret_cast<float*>(w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3]);
-  merge_rows<E, RPW, D, 16>(part0, (int64_t)t.tiles * Rc::BYTES, Rc::acc_off(w), Rc::m_off(w), Rc::l_off(w), t.splits,
+  merge_rows<E, RPW, D, (RPW == 16 ? 4 : 16)>(part0, (int64_t)t.tiles * Rc::BYTES, Rc::acc_off(w), Rc::m_off(w), Rc::l_off(w), t.splits,
                         min(RPW, t.C - t.row0), out0, (int64_t)p.hq * D, wl);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(p.p_cnt + t.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1296,6 +1532,199 @@ DEV void prefill_tile_bf16(const PodParams& p, int task, const LdsBufs& lb) {
   prefill_finish_split<Bf16, D, C::RPW>(p, t, task, lb);
 }
 
+// bf16 prefill tile of the four-workgroups-per-CU envelope (at most 128
+// registers per lane, 40 KB of LDS per workgroup): 16 query rows of one
+// head per wave on v_mfma_f32_16x16x32_bf16, the same 32-key blocks and
+// LDS-DMA staging as the 32-row tile but through two stages, one block
+// ahead.  Per block:
+//   S^T[key, row] = K Q^T      two 16-key tiles x D/32 k-steps; A = K rows
+//                              from LDS, B = Q^T in registers;
+//   O^T[d, row] += V^T P^T     D/16 d tiles, the block's 32 keys as k; A =
+//                              V^T from two transposing reads (keys 4q..4q+3
+//                              and 16+4q..16+4q+3), B = P^T straight from the
+//                              S^T accumulators (the key order is permuted
+//                              the same way on both sides).
+// Lane l holds row l & 15; the four lanes of a row (quads q = l >> 4) hold
+// different keys and share the running maximum, raised lazily as in the
+// 32-row tile.
+template <int D>
+struct PfBf16x4 {
+  static constexpr int RPW = 16;                     // query rows per wave
+  static constexpr int BN = PfBf16<D>::BN;           // keys per staged block
+  static constexpr int ROWB = D * 2;
+  static constexpr int OPB = BN * ROWB;              // bytes per operand per stage
+  static constexpr int STAGE = 2 * OPB;              // K block then V block
+  static constexpr int CH = D / 8;
+  static_assert(2 * DecMfma4<D>::LDS_WAVE <= STAGE, "two decode waves share a stage buffer");
+};
+
+template <int D>
+DEV void prefill_tile_bf16x4(const PodParams& p, int task, const LdsBufs& lb) {
+  using C = PfBf16x4<D>;
+  constexpr int KC = D / 32;   // QK k-steps
+  constexpr int DT = D / 16;   // 16-wide d tiles of O^T
+  const TaskGeom t = prefill_geom<C::RPW>(p, task);
+  const int lane = lane_id();
+  const int q4 = lane >> 4, rl = lane & 15;
+  const int row = t.row0 + rl;
+  const int64_t tok_bytes = (int64_t)p.hkv * D * 2;
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)t.g * D * 2;
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)t.g * D * 2;
+  char* stg[2] = {lb.st[0], lb.st[2]};
+
+  // Q^T operand: lane holds d = 32c + 8 q4 .. +8 of its row
+  bf16x8_t qf[KC];
+  {
+    const char* qrow =
+        reinterpret_cast<const char*>(p.qp) + (((int64_t)(t.row_base + row) * p.hq + t.head) * D + 8 * q4) * 2;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < t.C) v = *reinterpret_cast<const uint4*>(qrow + c * 64);
+      qf[c] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.0f;
+
+  const int nblk = t.k1 > t.k0 ? (t.k1 - t.k0 + C::BN - 1) / C::BN : 0;
+  const int lim = t.P0 + row;  // last visible key of this lane's row
+
+  int* pids = lb.pids;
+  const int pg0 = t.k0 / kPageSize;
+  const int pg1 = min((t.Lp + kPageSize - 1) / kPageSize, (t.k0 + nblk * C::BN + kPageSize - 1) / kPageSize);
+  preload_page_ids(t.pt, p.num_pages, pg0, pg1 - pg0, pids);
+  __syncthreads();
+
+  if (nblk > 0) {
+    const PfDma<D> dma = prefill_dma_offsets<D, true>(tok_bytes);
+    auto kb_of = [&](int b) __attribute__((always_inline)) { return t.k0 + min(b, nblk - 1) * C::BN; };
+    prefill_issue_block<D, true>(kpool, vpool, tok_bytes,
+                                 __builtin_amdgcn_readfirstlane(pids[prefill_wave_page_index<D>(kb_of(0), t.Lp, pg0)]),
+                                 t.Lp, kb_of(0), dma, stg[0]);
+    int pid_next = pids[prefill_wave_page_index<D>(kb_of(1), t.Lp, pg0)];
+    // Per-lane operand offsets inside a stage.  K: row rl of each 16-key tile
+    // (the second tile 16 rows further: the swizzle depends on row & 15
+    // only), chunk 4c + q4.  V: key rows 4 q4 + tk and 16 + 4 q4 + tk,
+    // d = 16 dt + 4 tj .. +4.  Masked to 16 bits so that the stage base
+    // folds into the reads' immediate offsets.
+    uint32_t koff[KC], voff[DT];
+    const int tk = rl >> 2, tj = rl & 3;
+    const int vr0 = 4 * q4 + tk;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) koff[c] = (uint32_t)(rl * C::ROWB + (((4 * c + q4) ^ ksw_rows<C::CH>(rl)) << 4)) & 0xffffu;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      voff[dt] = (uint32_t)(C::OPB + vr0 * C::ROWB + (((2 * dt + (tj >> 1)) ^ vsw_decode<C::CH>(vr0)) << 4) + ((tj & 1) << 3)) & 0xffffu;
+    const float c2 = p.scale_log2;
+
+    for (int b = 0; b < nblk; ++b) {
+      // block b has landed (this wave's share) and, after the barrier, every
+      // wave's share; every wave is also done with block b - 1, whose stage
+      // the next DMA overwrites
+      wait_vm_lgkm<0>();
+      __builtin_amdgcn_s_barrier();
+      const int page = __builtin_amdgcn_readfirstlane(pid_next);
+      prefill_issue_block<D, true>(kpool, vpool, tok_bytes, page, t.Lp, kb_of(b + 1), dma, stg[(b + 1) & 1]);
+      pid_next = pids[prefill_wave_page_index<D>(kb_of(b + 2), t.Lp, pg0)];
+      const char* st = stg[b & 1];
+      const int kb0 = t.k0 + b * C::BN;
+      // S^T of the block's two 16-key tiles; one tile's K operands in
+      // registers at a time (the envelope has 128 registers per lane)
+      f32x4_t sc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sc[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        bf16x8_t ka[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) ka[c] = *reinterpret_cast<const bf16x8_t*>(st + koff[c] + tt * 16 * C::ROWB);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qf[c], sc[tt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if ((kb0 + C::BN - 1) > (t.P0 + t.row0)) {  // diagonal block: causal mask
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc[tt][j] = kb0 + 16 * tt + 4 * q4 + j <= lim ? sc[tt][j] : kNegInf;
+      }
+      float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+      mx = fmaxf(mx, fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      mx *= c2;  // scale > 0: the max commutes with it
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
+        const float mm = max_xor32(max_xor16(mx));
+        const float mnew = fmaxf(m, mm);
+        const float alpha = fast_exp2(m - safe_max(mnew));
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        m = mnew;
+      }
+      const float nmu = -safe_max(m);
+      uint32_t pw[4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          pw[2 * tt + q2] = pack_bf16(fast_exp2(fmaf(sc[tt][2 * q2], c2, nmu)), fast_exp2(fmaf(sc[tt][2 * q2 + 1], c2, nmu)));
+          // l sums the bf16 weights the PV product uses, so they normalise exactly
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[2 * tt + q2]), kOnes2, l, false);
+        }
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      // PV in groups of two d tiles (their V^T operands read together)
+      constexpr int DG = 2;
+#pragma unroll
+      for (int d0 = 0; d0 < DT; d0 += DG) {
+        bf16x8_t va[DG];
+#pragma unroll
+        for (int e = 0; e < DG; ++e) {
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(st + voff[d0 + e]));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(st + voff[d0 + e] + 16 * C::ROWB));
+          va[e] = __builtin_bit_cast(bf16x8_t, (short __attribute__((ext_vector_type(8)))){
+              lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+#pragma unroll
+        for (int e = 0; e < DG; ++e) o[d0 + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[e], pf, o[d0 + e], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vmem();  // no DMA may still target this workgroup's LDS when it is reused
+  }
+  __syncthreads();
+
+  const float ltot = sum_xor32(sum_xor16(l));
+  if (t.splits == 1) {
+    if (row < t.C) {
+      const float inv = 1.0f / ltot;
+      char* orow = reinterpret_cast<char*>(p.op) + (((int64_t)(t.row_base + row) * p.hq + t.head) * D + 4 * q4) * 2;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint2 w;
+        w.x = pack_bf16(o[dt][0] * inv, o[dt][1] * inv);
+        w.y = pack_bf16(o[dt][2] * inv, o[dt][3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * dt) = w;
+      }
+    }
+    return;
+  }
+  // split partial: unnormalised acc, m (base 2), l
+  using Rc = PfRec<D, C::RPW>;
+  const int w = wave_id();
+  const Rsrc rs = dev_rsrc(reinterpret_cast<const char*>(p.p_part) + (int64_t)task * Rc::BYTES, Rc::BYTES);
+  const uint32_t ro = Rc::acc_off(w) + rl * D * 4;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st_dev4(rs, ro + (16 * dt + 4 * q4) * 4, o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (q4 == 0) {
+    st_dev1(rs, Rc::m_off(w) + rl * 4, m);
+    st_dev1(rs, Rc::l_off(w) + rl * 4, ltot);
+  }
+  prefill_finish_split<Bf16, D, C::RPW>(p, t, task, lb);
+}
+
 // fp32 prefill tile (exact fp32, VALU): lane = one query row, K/V blocks of 32
 // keys in LDS read as broadcasts.
 template <int D>
@@ -1441,6 +1870,16 @@ constexpr int stage_bytes() {
   __shared__ int lds_pids[kMaxSplitKeys / kPageSize];                                    \
   __shared__ int lds_flag;                                                               \
   const LdsBufs lb{{lds_st0, lds_st1, lds_st2, lds_st3}, lds_pids, &lds_flag}
+
+// LDS of the four-workgroups-per-CU envelope: two prefill stages (each
+// also holding two decode waves' page buffers) and the split's page ids.
+#define POD_DECLARE_LDS4(D)                                                                          \
+  __shared__ __attribute__((aligned(16))) char lds4_s0[PfBf16x4<D>::STAGE];                          \
+  __shared__ __attribute__((aligned(16))) char lds4_s1[PfBf16x4<D>::STAGE];                          \
+  __shared__ int lds_pids[kMaxSplitKeys / kPageSize];                                                \
+  __shared__ int lds_flag;                                                                           \
+  const LdsBufs lb{{lds4_s0, lds4_s0 + PfBf16x4<D>::STAGE / 2, lds4_s1, lds4_s1 + PfBf16x4<D>::STAGE / 2}, \
+                   lds_pids, &lds_flag}
 
 // ------------------------------------------------------------------ kernels
 // Pages in flight per decode wave: the fused kernel keeps 2 WGs per CU, so its
@@ -1604,9 +2043,8 @@ DEV bool ticket_policy(const PodParams& p) {
 // A CU-balanced launch resident in one round (fixed_order) also hands out
 // roles by workgroup id -- one role's tasks first, then the other's -- with
 // no atomics in front of the work.
-template <class E, int D, int G>
-__global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
-  POD_DECLARE_LDS(E, D);
+template <class RunP, class RunD>
+DEV void fused_body(const PodParams& p, RunP&& run_prefill, RunD&& run_decode) {
   __shared__ int role_task[4];
   __shared__ uint32_t cu_word;
   if (threadIdx.x == 0) {
@@ -1635,14 +2073,54 @@ __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   const int role = role_task[0], task = role_task[1];
   if (role_task[3] && ticket_policy(p)) clear_tickets(p);
   if (role == 0) {
-    if (task < p.p_tasks) PfSel<E, D>::run(p, task, lb);
+    if (task < p.p_tasks) run_prefill(task);
   } else {
-    if (task < p.d_wg_tasks) decode_wg<E, D, G, fused_pf<E, G>()>(p, task, lb);
+    if (task < p.d_wg_tasks) run_decode(task);
   }
   if (role_task[2]) {
     __syncthreads();
     if (threadIdx.x == 0) atomicSub(p.tickets + cu_word, role == 0 ? 1u : 0x10000u);
   }
+}
+
+template <class E, int D, int G>
+__global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
+  POD_DECLARE_LDS(E, D);
+  fused_body(
+      p, [&](int task) { PfSel<E, D>::run(p, task, lb); },
+      [&](int task) { decode_wg<E, D, G, fused_pf<E, G>()>(p, task, lb); });
+}
+
+// The three launches of the four-workgroups-per-CU envelope (bf16 only).
+template <int D, int G>
+__global__ __launch_bounds__(256, 4) void pod_hybrid4_kernel(PodParams p) {
+  POD_DECLARE_LDS4(D);
+  fused_body(
+      p,
+      [&](int task) {
+        if (p.prefill_priority) __builtin_amdgcn_s_setprio(1);
+        prefill_tile_bf16x4<D>(p, task, lb);
+        __builtin_amdgcn_s_setprio(0);
+      },
+      [&](int task) { decode_wg4<D, G>(p, task, lb); });
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 4) void pod_prefill4_kernel(PodParams p) {
+  POD_DECLARE_LDS4(D);
+  prefill_tile_bf16x4<D>(p, blockIdx.x, lb);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 4) void pod_decode4_kernel(PodParams p) {
+  constexpr int W = DecMfma4<D>::LDS_WAVE;
+  __shared__ __attribute__((aligned(16))) char dbuf0[W];
+  __shared__ __attribute__((aligned(16))) char dbuf1[W];
+  __shared__ __attribute__((aligned(16))) char dbuf2[W];
+  __shared__ __attribute__((aligned(16))) char dbuf3[W];
+  __shared__ int dpids[kWavesPerWG * kSplitIdRegs * 64];
+  const LdsBufs lb{{dbuf0, dbuf1, dbuf2, dbuf3}, dpids, nullptr};
+  decode_wg4<D, G>(p, blockIdx.x, lb);
 }
 
 // Persistent variant of the fused kernel: a grid of (CUs x resident
@@ -1686,6 +2164,23 @@ __global__ __launch_bounds__(256, 2) void pod_persistent_kernel(PodParams p) {
 template <class E, int D, int G>
 static int launch_t(int which, const PodParams& p, const Plan& pl, hipStream_t s) {
   const dim3 block(256);
+  if (pl.wg_per_cu == 4) {
+    if constexpr (E::bytes == 2) {
+      switch (which) {
+        case kKernelHybrid:
+          hipLaunchKernelGGL((pod_hybrid4_kernel<D, G>), dim3(pl.grid), block, 0, s, p);
+          break;
+        case kKernelPrefill:
+          hipLaunchKernelGGL((pod_prefill4_kernel<D, G>), dim3(pl.p_tasks), block, 0, s, p);
+          break;
+        default:
+          hipLaunchKernelGGL((pod_decode4_kernel<D, G>), dim3(pl.d_wg_tasks), block, 0, s, p);
+          break;
+      }
+      return (int)hipGetLastError();
+    }
+    return (int)hipErrorInvalidValue;
+  }
   switch (which) {
     case kKernelHybrid:
       if (pl.persistent)

@@ -28,8 +28,8 @@ int check_shape(const Shape& s) {
   return POD_OK;
 }
 
-static void tile_geometry(const Shape& s, int& rpw, int& hpt, int& row_waves, int& rpt, int& hgroups) {
-  rpw = rows_per_wave(s.dtype);
+static void tile_geometry(const Shape& s, int wg, int& rpw, int& hpt, int& row_waves, int& rpt, int& hgroups) {
+  rpw = rows_per_wave(s.dtype, wg);
   hpt = std::min(s.G, kWavesPerWG);
   row_waves = kWavesPerWG / hpt;
   rpt = rpw * row_waves;
@@ -37,16 +37,29 @@ static void tile_geometry(const Shape& s, int& rpw, int& hpt, int& row_waves, in
 }
 
 void derive_capacities(const Shape& s, Limits& lim) {
-  int rpw, hpt, rw, rpt, hg;
-  tile_geometry(s, rpw, hpt, rw, rpt, hg);
-  const int64_t slots = (int64_t)lim.num_cus * lim.wg_per_cu;
-  // max_chunk_len bounds the rows of all chunks of a call; each chunk but
-  // the first may add one partial row block
-  const int64_t rows = std::max(1, lim.max_chunk_len);
-  lim.cap_tiles = (ceil_div(rows, rpt) + std::min<int64_t>(kMaxChunks, rows) - 1) * s.hkv * hg;
-  lim.cap_prefill_tasks = std::max<int64_t>(
-      {1, lim.cap_waves * slots + lim.cap_tiles,
-       lim.cap_tiles * ceil_div(std::max(1, lim.max_context), kMaxSplitKeys)});
+  // the largest counts over the envelopes this handle may plan with
+  lim.cap_tiles = 0;
+  lim.cap_prefill_tasks = 1;
+  lim.cap_rowhead_tasks = 0;
+  for (int wg : {2, 4}) {
+    if (!envelope_allowed(s.dtype, lim.wg_per_cu, wg)) continue;
+    int rpw, hpt, rw, rpt, hg;
+    tile_geometry(s, wg, rpw, hpt, rw, rpt, hg);
+    const int64_t slots = (int64_t)lim.num_cus * wg;
+    // max_chunk_len bounds the rows of all chunks of a call; each chunk but
+    // the first may add one partial row block
+    const int64_t rows = std::max(1, lim.max_chunk_len);
+    const int64_t tiles = (ceil_div(rows, rpt) + std::min<int64_t>(kMaxChunks, rows) - 1) * s.hkv * hg;
+    const int64_t finest = ceil_div(std::max(1, lim.max_context),
+                                    s.dtype == kBf16 ? kMinPrefillSplitKeys : kMinPrefillSplitKeysF32);
+    int64_t tasks = std::max<int64_t>({1, std::max(lim.cap_waves, 2) * slots + tiles,
+                                       tiles * ceil_div(std::max(1, lim.max_context), kMaxSplitKeys)});
+    if (lim.cap_waves < 0) tasks = std::max(tasks, tiles * finest);
+    if (lim.prefill_splits > 0) tasks = std::max(tasks, tiles * std::min<int64_t>(lim.prefill_splits, finest));
+    lim.cap_tiles = std::max(lim.cap_tiles, tiles);
+    lim.cap_prefill_tasks = std::max(lim.cap_prefill_tasks, tasks);
+    lim.cap_rowhead_tasks = std::max<int64_t>(lim.cap_rowhead_tasks, tasks * rpw * kWavesPerWG);
+  }
   int64_t total = lim.max_total_context > 0 ? lim.max_total_context
                                             : (int64_t)lim.max_num_decode * lim.max_context;
   lim.cap_wave_tasks =
@@ -66,8 +79,7 @@ WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim) {
   w.d_cnt = at;
   at = align(at + (size_t)std::max(1, lim.max_num_decode) * s.hkv * 4);
   w.p_part = at;
-  const size_t rowheads = (size_t)rows_per_wave(s.dtype) * kWavesPerWG;
-  at = align(at + (size_t)lim.cap_prefill_tasks * rowheads * (s.d + 2) * 4);
+  at = align(at + (size_t)lim.cap_rowhead_tasks * (s.d + 2) * 4);
   w.d_part = at;
   const int G = s.hq / s.hkv;
   const size_t rec = ((size_t)G * (s.d + 2) + 3) & ~size_t(3);  // 16-byte records
@@ -82,6 +94,7 @@ WorkspaceLayout workspace_layout_for_plan(const Shape& s, const Plan& pl) {
   bool split = false;
   for (int k = 0; pl.has_p && k < pl.n_chunks; ++k) split |= pl.ch[k].splits > 1;
   lim.cap_prefill_tasks = split ? pl.p_tasks : 0;  // partials only where tiles are split
+  lim.cap_rowhead_tasks = lim.cap_prefill_tasks * pl.rows_per_wave * kWavesPerWG;
   lim.max_num_decode = pl.has_d ? pl.N : 0;
   lim.cap_wave_tasks = pl.has_d ? pl.d_wave_tasks : 0;
   return workspace_layout(s, lim);
@@ -95,15 +108,16 @@ static void reduce_share(int64_t a, int64_t b, int& num, int& den) {
   den = kShareDen;
 }
 
-int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, const DecodeIn& d,
-              Plan* out) {
+// Plan one call for the envelope of `wg` co-resident workgroups per CU.
+static int plan_wg(const Shape& s, const Limits& lim, int wg, int mode, const PrefillIn& p, const DecodeIn& d,
+                   Plan* out) {
   if (!out) return POD_ERR_INVALID_ARG;
   int rc = check_shape(s);
   if (rc) return rc;
   Plan pl;
   pl.mode = mode;
   pl.num_cus = lim.num_cus;
-  pl.wg_per_cu = lim.wg_per_cu;
+  pl.wg_per_cu = wg;
   pl.policy = lim.policy;
   if (lim.num_cus <= 0) return POD_ERR_INVALID_ARG;
 
@@ -117,7 +131,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
   pl.has_p = want_p && p.present;
   pl.has_d = want_d && d.present;
 
-  const int64_t slots = (int64_t)lim.num_cus * lim.wg_per_cu;
+  const int64_t slots = (int64_t)lim.num_cus * wg;
 
   if (pl.has_p) {
     if (p.n < 1 || p.n > kMaxChunks || p.stride < 0) return POD_ERR_INVALID_ARG;
@@ -132,7 +146,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
       order[c] = c;
     }
     if (rows > lim.max_chunk_len) return POD_ERR_INVALID_ARG;
-    tile_geometry(s, pl.rows_per_wave, pl.heads_per_tile, pl.row_waves, pl.rows_per_tile,
+    tile_geometry(s, wg, pl.rows_per_wave, pl.heads_per_tile, pl.row_waves, pl.rows_per_tile,
                   pl.head_groups);
     // Tasks run chunk by chunk, the longest key range first (its tiles take
     // longest), the caller's order among equals.
@@ -159,18 +173,25 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     pl.tiles = (int)tiles;
     const int bn = keys_per_block(s.dtype);
     // KV splits.  When the tiles do not fill the machine, the average tile
-    // is split s_par ways (at most cap_waves waves of workgroups in all) and
+    // is split s_par ways -- enough for one wave of workgroups, and at most
+    // cap_waves waves in all (paper §4.2.3 caps chunked-prefill splits at
+    // two waves so that the prefill cannot crowd out the decodes) -- and
     // each chunk in proportion to its key range, so tasks carry similar
     // numbers of keys; a split added for parallelism keeps at least
-    // min_keys keys, and no split exceeds kMaxSplitKeys (its page
-    // ids are staged in LDS).
+    // min_keys keys, and no split exceeds kMaxSplitKeys (its page ids are
+    // staged in LDS).  Without the cap (cap_waves < 0) every tile is split
+    // as finely as min_keys allows; prefill_splits > 0 fixes the count.
     const int min_keys = s.dtype == kBf16 ? kMinPrefillSplitKeys : kMinPrefillSplitKeysF32;
     auto assign = [&](int64_t s_par) {
       int64_t tasks = 0;
       for (int k = 0; k < p.n; ++k) {
         ChunkPlan& ch = pl.ch[k];
         int64_t sp = 1;
-        if (s_par > 1) {
+        if (lim.prefill_splits > 0) {
+          sp = std::min<int64_t>(lim.prefill_splits, ceil_div(ch.Lp, min_keys));
+        } else if (lim.cap_waves < 0) {
+          sp = ceil_div(ch.Lp, min_keys);
+        } else if (s_par > 1) {
           sp = (int64_t)std::floor((double)s_par * (double)tiles * ch.Lp / work);
           sp = std::max<int64_t>(1, std::min<int64_t>(sp, ceil_div(ch.Lp, min_keys)));
         }
@@ -183,7 +204,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
       return tasks;
     };
     int64_t s_par = 1;
-    if (tiles < slots)
+    if (tiles < slots && lim.cap_waves > 0)
       s_par = std::max<int64_t>(1, std::min<int64_t>(ceil_div(slots, tiles), lim.cap_waves * slots / tiles));
     int64_t tasks = assign(s_par);
     if (tasks > lim.cap_prefill_tasks) tasks = assign(1);
@@ -248,16 +269,18 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     }
     const double t_p = std::max(t_task, f_p / (s.dtype == kBf16 ? kPrefillFlopsBf16 : kPrefillFlopsF32));
     const double t_d = 2.0 * s.hkv * s.d * es * (double)pl.d_total / kDecodeBytesPerS;
+    pl.t_prefill = t_p;
+    pl.t_decode = t_d;
     if (lim.slots_x256 > 0)
-      pl.cu_prefill_x256 = lim.slots_x256;
+      pl.cu_prefill_x256 = std::min(lim.slots_x256, 256 * wg);
     else if (t_p >= t_d)
-      pl.cu_prefill_x256 = 256 * lim.wg_per_cu;
+      pl.cu_prefill_x256 = 256 * wg;
     else if (2.75 * t_p < t_d)
       pl.cu_prefill_x256 = 0;
     else if (t_d >= kOverlapMinSeconds)
-      pl.cu_prefill_x256 = 352;
+      pl.cu_prefill_x256 = 176 * wg;  // 1.375 of 2 slots
     else
-      pl.cu_prefill_x256 = (int)std::max<int64_t>(1, std::min<int64_t>(256, 256LL * pl.p_tasks / lim.num_cus));
+      pl.cu_prefill_x256 = (int)std::max<int64_t>(1, std::min<int64_t>(128 * wg, 256LL * pl.p_tasks / lim.num_cus));
   }
 
   if (pl.has_d) {
@@ -273,6 +296,7 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     std::vector<int> lens(d.ctx_host, d.ctx_host + d.N);
     std::nth_element(lens.begin(), lens.begin() + d.N / 2, lens.end());
     const int64_t median = lens[d.N / 2];
+    pl.d_median = (int)median;
     const int64_t target = (int64_t)lim.num_cus * 5;
     int64_t T = round_up(std::min(ceil_div(pl.d_total * s.hkv, target), median), kPageSize);
     T = std::min<int64_t>(kMaxSplitTokens, std::max<int64_t>(min_split_tokens(s.dtype, lim.max_context), T));
@@ -329,6 +353,33 @@ int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, c
     pl.share_den = 1;
   }
   *out = pl;
+  return POD_OK;
+}
+
+int make_plan(const Shape& s, const Limits& lim, int mode, const PrefillIn& p, const DecodeIn& d, Plan* out) {
+  if (lim.wg_per_cu == 2 || lim.wg_per_cu == 4) return plan_wg(s, lim, lim.wg_per_cu, mode, p, d, out);
+  // Runtime choice between the envelopes (paper §4.2.2 and §5.4.1 pick two
+  // or four CTAs per SM per batch).  Measured on MI355X with these tiles:
+  // the 16-row prefill tile of the four-workgroup envelope runs 1.3-1.6x
+  // slower than the 32-row tile (the same LDS and DMA bytes per block for
+  // half the FLOPs), so every hybrid batch tried -- prefill- and
+  // decode-dominated, short and long contexts -- was faster with two
+  // workgroups per CU; decode alone was 2-5% faster with four when all its
+  // workgroups start in one round of four per CU, and slower when it takes
+  // several.  So: four for a call without prefill whose decode workgroups
+  // fit one round of four per CU, two otherwise (and always for fp32 and
+  // the persistent grid, which have only that envelope).
+  Plan p2;
+  int rc = plan_wg(s, lim, 2, mode, p, d, &p2);
+  if (rc) return rc;
+  if (envelope_allowed(s.dtype, 0, 4) && !lim.persistent && p2.has_d && !p2.has_p) {
+    Plan p4;
+    if (plan_wg(s, lim, 4, mode, p, d, &p4) == POD_OK && (int64_t)p4.d_wg_tasks <= (int64_t)lim.num_cus * 4) {
+      *out = p4;
+      return POD_OK;
+    }
+  }
+  *out = p2;
   return POD_OK;
 }
 

@@ -68,13 +68,17 @@ struct Shape {
 struct Limits {
   int max_chunk_len = 0, max_num_decode = 0, max_context = 0;
   int64_t max_total_context = 0;
-  int wg_per_cu = 2, cap_waves = 2, policy = kPolicyCuBalanced;
+  int wg_per_cu = 2;  // co-resident workgroups per CU: 2, 4, or 0 (chosen per batch)
+  int cap_waves = 2;  // prefill tasks added for parallelism fill at most this many waves; -1: no cap
+  int prefill_splits = 0;  // KV splits per prefill tile; 0: from the batch
+  int policy = kPolicyCuBalanced;
   int slots_x256 = 0;  // prefill slots per CU for the CU-balanced policy; 0: from the batch
   int split_tokens = 0;  // decode tokens per wave task; 0: from the batch
   bool persistent = false;  // fused launch as a resident grid looping over the queues
   int num_cus = 0;
-  // capacities derived by workspace_layout()
+  // capacities derived by derive_capacities()
   int64_t cap_prefill_tasks = 0, cap_wave_tasks = 0, cap_tiles = 0;
+  int64_t cap_rowhead_tasks = 0;  // prefill tasks x row-heads per task (split partials)
 };
 
 // Prefill chunks of one call in the caller's order.  stride: page-table
@@ -112,6 +116,7 @@ struct Plan {
   bool has_d = false;
   int N = 0, T = 0, d_wave_tasks = 0, d_wg_tasks = 0;
   int d_max = 0;        // longest decode context
+  int d_median = 0;     // median decode context
   int64_t d_total = 0;  // sum of decode contexts
   int d_full = 0;       // decode units that are full T-token splits
   // fused scheduling
@@ -119,10 +124,18 @@ struct Plan {
   bool persistent = false;  // the fused launch is a resident grid of workgroups
   int fixed_order = 0;  // 0: roles claimed; 1 / 2: prefill / decode tasks by workgroup id first (no claims)
   int prefill_priority = 1;  // issue priority of prefill waves beside decode waves (0 or 1)
+  double t_prefill = 0.0, t_decode = 0.0;  // each role's time alone, as estimated for the role mix
 };
 
-// Rows of one wave's query block and keys per staged KV block, per dtype.
-inline int rows_per_wave(int dtype) { return dtype == kBf16 ? 32 : 64; }
+// Rows of one wave's query block and keys per staged KV block, per dtype
+// and resource envelope (2 or 4 workgroups per CU; fp32 has only 2).
+inline int rows_per_wave(int dtype, int wg) { return dtype == kBf16 ? (wg == 4 ? 16 : 32) : 64; }
+// The envelopes a handle may plan with (wg_per_cu 0 allows both for bf16).
+inline bool envelope_allowed(int dtype, int wg_config, int wg) {
+  if (wg == 4 && dtype != kBf16) return false;
+  return wg_config == 0 ? (wg == 2 || wg == 4) : wg == wg_config;
+}
+
 inline int keys_per_block(int dtype) { return dtype == kBf16 ? 64 : 32; }
 
 // 0 if (dtype, G, d, page) is built, else the status code to return.

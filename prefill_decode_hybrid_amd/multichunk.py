@@ -45,6 +45,8 @@ def main(argv=None):
     ap.add_argument("--policy", type=int, default=0)
     ap.add_argument("--slots-x256", type=int, default=0,
                     help="CU-balanced policy: prefill workgroups per CU in 1/256 (0: the planner's choice)")
+    ap.add_argument("--wg-per-cu", type=int, default=2,
+                    help="resource envelope: 2 or 4 workgroups per CU, 0 chosen per call")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
@@ -65,7 +67,8 @@ def main(argv=None):
     b = inputs.make_batch(spec, seed=a.seed)
     dev = b.to("cuda:0")
     ctx = b.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(b, policy=a.policy, prefill_slots_x256=a.slots_x256))
+    att = pod.PodAttention(pod.config_for_batch(b, policy=a.policy, prefill_slots_x256=a.slots_x256,
+                                                wg_per_cu=a.wg_per_cu))
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     op, od = torch.empty_like(dev.q_prefill), torch.empty_like(dev.q_decode)

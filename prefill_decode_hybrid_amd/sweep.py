@@ -12,7 +12,8 @@ would.  Each chunk's fused result is also compared bit for bit with the split
 launches.
 
     python -m prefill_decode_hybrid_amd.sweep --prompt 16384 --chunk 512 \\
-        --num-decode 64 --decode-context 16384 [--last 4] [--split-cap 0]
+        --num-decode 64 --decode-context 16384 [--last 4] [--split-cap 0] \\
+        [--prefill-splits 0] [--wg-per-cu 2]
 
 Prints one JSON line per run: per-chunk medians and the totals over the
 prompt.
@@ -37,7 +38,12 @@ def main(argv=None):
     ap.add_argument("--head-dim", type=int, default=128)
     ap.add_argument("--last", type=int, default=0, help="time only the last N chunks (0: all)")
     ap.add_argument("--split-cap", type=int, default=0,
-                    help="prefill split cap in waves of resident workgroups (0: the default, 2)")
+                    help="prefill split cap in waves of resident workgroups (0: the default, 2; -1: no cap)")
+    ap.add_argument("--prefill-splits", type=int, default=0,
+                    help="KV splits per prefill tile (0: the planner's choice)")
+    ap.add_argument("--wg-per-cu", type=int, default=2,
+                    help="resource envelope: 2 or 4 workgroups per CU, 0 chosen per call (the fused and "
+                         "split calls may then pick different envelopes and differ in rounding)")
     ap.add_argument("--policy", type=int, default=0)
     ap.add_argument("--slots-x256", type=int, default=0,
                     help="CU-balanced policy: prefill workgroups per CU in 1/256 (0: the planner's choice)")
@@ -67,7 +73,8 @@ def main(argv=None):
     dev = full.to("cuda:0")
     ctx_host = full.context_lens.clone().contiguous()
     cfg = pod.config_for_batch(full, policy=a.policy, prefill_split_cap_waves=a.split_cap,
-                               prefill_slots_x256=a.slots_x256, decode_split_tokens=a.split_tokens)
+                               prefill_slots_x256=a.slots_x256, decode_split_tokens=a.split_tokens,
+                               prefill_splits=a.prefill_splits, wg_per_cu=a.wg_per_cu)
     att = pod.PodAttention(cfg)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
@@ -103,14 +110,15 @@ def main(argv=None):
         rows.append({"chunk": i, "offset": p0, "fused_us": round(med[0], 1), "serial_us": round(med[1], 1),
                      "two_stream_us": round(med[2], 1), "prefill_tasks": plan["prefill_tasks"],
                      "prefill_splits": plan["prefill_splits"], "cu_prefill_x256": plan["cu_prefill_x256"],
-                     "decode_split_tokens": plan["decode_split_tokens"],
+                     "decode_split_tokens": plan["decode_split_tokens"], "wg_per_cu": plan["wg_per_cu"],
                      "fused_equals_split": same})
         print(f"[sweep] chunk {i} @ {p0}: fused {med[0]:.1f} serial {med[1]:.1f} streams {med[2]:.1f} us "
               f"(splits {plan['prefill_splits']}, x256 {plan['cu_prefill_x256']})", file=sys.stderr, flush=True)
     tot = {k: round(sum(r[k] for r in rows), 1) for k in ("fused_us", "serial_us", "two_stream_us")}
     out = {"sweep": "chunked prefill beside a fixed decode batch", "prompt": a.prompt, "chunk": a.chunk,
            "num_decode": a.num_decode, "decode_context": a.decode_context, "heads": [a.num_q_heads, a.num_kv_heads],
-           "head_dim": a.head_dim, "chunks_timed": len(rows), "split_cap_waves": a.split_cap or 2,
+           "head_dim": a.head_dim, "chunks_timed": len(rows), "split_cap_waves": a.split_cap or 2, "prefill_splits": a.prefill_splits,
+           "wg_per_cu": a.wg_per_cu,
            "policy": a.policy, "slots_x256": a.slots_x256, "split_tokens": a.split_tokens, "steps": a.steps, "totals": tot,
            "speedup_vs_serial": round(tot["serial_us"] / tot["fused_us"], 4),
            "speedup_vs_two_stream": round(tot["two_stream_us"] / tot["fused_us"], 4),

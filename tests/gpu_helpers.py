@@ -23,6 +23,9 @@ class Run:
     """A batch on cuda:0 plus a handle sized for it."""
 
     def __init__(self, batch, **cfg_kw):
+        # one resource envelope for every entry point unless a test asks
+        # otherwise, so that fused and split launches run the same tiles
+        cfg_kw.setdefault("wg_per_cu", 2)
         self.cpu = batch
         self.dev = batch.to("cuda:0")
         self.cfg = pod.config_for_batch(batch, **cfg_kw)

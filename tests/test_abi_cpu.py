@@ -60,7 +60,7 @@ def _cfg(spec, **kw):
     base = dict(dtype=pod.POD_BF16 if spec["dtype"] == "bf16" else pod.POD_F32,
                 num_q_heads=spec["num_q_heads"], num_kv_heads=spec["num_kv_heads"],
                 head_dim=spec["head_dim"], max_chunk_len=4096, max_num_decode=512,
-                max_context=32768, max_total_context=4 << 20)
+                max_context=32768, max_total_context=4 << 20, wg_per_cu=2)
     base.update(kw)
     return pod.make_config(**base)
 
@@ -234,7 +234,7 @@ def test_validation_null_pointers():
 
 @pytest.mark.parametrize("kw", [dict(head_dim=96), dict(num_q_heads=24, num_kv_heads=8),
                                 dict(page_size=8), dict(dtype=pod.POD_F32, head_dim=128),
-                                dict(num_q_heads=32, num_kv_heads=2), dict(wg_per_cu=4),
+                                dict(num_q_heads=32, num_kv_heads=2), dict(dtype=pod.POD_F32, head_dim=64, wg_per_cu=4),
                                 dict(max_context=261889)])
 def test_unsupported_shapes(kw):
     cfg = _cfg(2, **kw)
@@ -359,3 +359,80 @@ def test_fp32_decode_splits_and_the_split_limit():
     with pytest.raises(pod.PodAttnError):
         plan(_cfg(1, max_context=200000, decode_split_tokens=64), pod.MODE_DECODE, None, _decode([37]))
     assert plan(_cfg(1, decode_split_tokens=64), pod.MODE_DECODE, None, _decode([37]))["decode_split_tokens"] == 64
+
+
+def test_envelope_validation(lib):
+    # workgroups per CU: 0 (chosen per call), 2 or 4; the four-workgroup
+    # envelope is bf16 only and has no persistent grid
+    for wg, dtype, persistent, want in [(3, pod.POD_BF16, 0, pod.POD_ERR_INVALID_ARG),
+                                        (8, pod.POD_BF16, 0, pod.POD_ERR_INVALID_ARG),
+                                        (4, pod.POD_F32, 0, pod.POD_ERR_UNSUPPORTED),
+                                        (4, pod.POD_BF16, 1, pod.POD_ERR_UNSUPPORTED)]:
+        cfg = pod.make_config(dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=64, wg_per_cu=wg,
+                              persistent=persistent)
+        with pytest.raises(pod.PodAttnError) as e:
+            pod.pod_attn_plan(cfg, 256, pod.MODE_DECODE, None, _decode([100]))
+        assert e.value.status == want, (wg, dtype, persistent)
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_four_workgroup_plan(cid):
+    # 16-row prefill tiles (four heads of a kv head per tile, or more rows
+    # for smaller groups), splits and slots counted in waves of 4 per CU
+    spec = inputs.CONFIGS[cid]
+    lens = inputs.draw_context_lens(cid, 0)
+    C, P0 = spec["chunk_len"], spec["chunk_offset"]
+    hq, hkv = spec["num_q_heads"], spec["num_kv_heads"]
+    G = hq // hkv
+    st = plan(_cfg(cid, wg_per_cu=4), pod.MODE_HYBRID, _prefill(C, P0), _decode(lens))
+    assert st["wg_per_cu"] == 4
+    assert st["prefill_rows_per_tile"] * st["prefill_heads_per_tile"] == 16 * 4
+    assert st["prefill_tiles"] == -(-C // st["prefill_rows_per_tile"]) * hkv * (G // st["prefill_heads_per_tile"])
+    assert st["prefill_tasks"] == st["prefill_tiles"] * st["prefill_splits"]
+    if st["prefill_splits"] > -(-(C + P0) // 16384):
+        assert st["prefill_tasks"] <= 2 * 4 * 256
+    T = st["decode_split_tokens"]
+    assert st["decode_wave_tasks"] == hkv * sum(-(-int(L) // T) for L in lens)
+    assert st["grid"] == st["prefill_tasks"] + st["decode_wg_tasks"]
+    assert 0 <= st["cu_prefill_x256"] <= 4 * 256
+    # the decode split is the same as in the two-workgroup envelope
+    st2 = plan(_cfg(cid), pod.MODE_HYBRID, _prefill(C, P0), _decode(lens))
+    assert st2["wg_per_cu"] == 2 and st2["decode_split_tokens"] == T
+
+
+@pytest.mark.parametrize("cid,decode_alone", [(1, 2), (2, 4), (3, 4), (4, 2), (5, 4)])
+def test_runtime_envelope_choice(cid, decode_alone):
+    # hybrid and prefill calls keep two workgroups per CU; a decode-only call
+    # takes four when its workgroups all start in one round of four per CU
+    # (the Llama, long-context and prefill-heavy batches' decodes), two when
+    # they take several (the decode-heavy batch) and for fp32
+    spec = inputs.CONFIGS[cid]
+    lens = inputs.draw_context_lens(cid, 0)
+    pa = _prefill(spec["chunk_len"], spec["chunk_offset"])
+    assert plan(_cfg(cid, wg_per_cu=0), pod.MODE_HYBRID, pa, _decode(lens))["wg_per_cu"] == 2
+    assert plan(_cfg(cid, wg_per_cu=0), pod.MODE_PREFILL, pa, None)["wg_per_cu"] == 2
+    st = plan(_cfg(cid, wg_per_cu=0), pod.MODE_DECODE, None, _decode(lens))
+    assert st["wg_per_cu"] == decode_alone
+    if decode_alone == 4:
+        assert st["decode_wg_tasks"] <= 4 * 256
+    # a hybrid call without its prefill half runs the decode alone, and chooses as such
+    assert plan(_cfg(cid, wg_per_cu=0), pod.MODE_HYBRID, None, _decode(lens))["wg_per_cu"] == decode_alone
+
+
+def test_prefill_split_knobs():
+    # the last 512-token chunk of a 16K prompt beside 64 decodes of 16K
+    # (the split-limiting study's shape): one wave of tasks by default,
+    # finest splits without the cap, or a fixed count
+    pa, da = _prefill(512, 15872), _decode([16384] * 64)
+    st = plan(_cfg(3), pod.MODE_HYBRID, pa, da)
+    assert st["prefill_tasks"] <= 512
+    st = plan(_cfg(3, prefill_split_cap_waves=-1), pod.MODE_HYBRID, pa, da)
+    assert st["prefill_splits"] == 16 and st["prefill_split_keys"] == 1024
+    for n in (1, 3, 8):
+        st = plan(_cfg(3, prefill_splits=n), pod.MODE_HYBRID, pa, da)
+        assert st["prefill_splits"] == n
+        assert st["prefill_tasks"] == st["prefill_tiles"] * n
+    for bad in (dict(prefill_split_cap_waves=-2), dict(prefill_splits=-1)):
+        with pytest.raises(pod.PodAttnError) as e:
+            plan(_cfg(3, **bad), pod.MODE_HYBRID, pa, da)
+        assert e.value.status == pod.POD_ERR_INVALID_ARG

@@ -91,7 +91,7 @@ def test_persistent_several_chunks():
     ctx = b.context_lens.clone().contiguous()
     outs = []
     for persistent in (0, 1):
-        att = pod.PodAttention(pod.config_for_batch(b, persistent=persistent))
+        att = pod.PodAttention(pod.config_for_batch(b, persistent=persistent, wg_per_cu=2))
         try:
             op, od = torch.empty_like(dev.q_prefill), torch.empty_like(dev.q_decode)
             att.hybrid_varlen(dev, op, od, ctx)

@@ -33,7 +33,7 @@ def test_chunks_of_one_prompt_match_oracle():
     full = inputs.make_batch(spec, seed=5)
     dev = full.to("cuda:0")
     ctx = full.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(full))
+    att = pod.PodAttention(pod.config_for_batch(full, wg_per_cu=2))
     try:
         for p0 in range(0, prompt, C):
             n = min(C, prompt - p0)

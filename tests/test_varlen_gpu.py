@@ -89,7 +89,7 @@ def test_varlen_matches_oracle(sp):
     b = inputs.make_batch(sp, seed=2)
     dev = b.to("cuda:0")
     ctx = b.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(b))
+    att = pod.PodAttention(pod.config_for_batch(b, wg_per_cu=2))
     try:
         op = torch.full_like(dev.q_prefill, float("nan"))
         od = torch.full_like(dev.q_decode, float("nan"))
@@ -115,7 +115,7 @@ def test_varlen_policies_bitwise(policy):
     ctx = b.context_lens.clone().contiguous()
     outs = []
     for pol in (pod.POD_POLICY_CU_BALANCED, policy):
-        att = pod.PodAttention(pod.config_for_batch(b, policy=pol))
+        att = pod.PodAttention(pod.config_for_batch(b, policy=pol, wg_per_cu=2))
         try:
             op, od = torch.empty_like(dev.q_prefill), torch.empty_like(dev.q_decode)
             att.hybrid_varlen(dev, op, od, ctx)
@@ -132,7 +132,7 @@ def test_one_chunk_varlen_equals_single_chunk_call():
     b = inputs.make_batch(sp, seed=6)
     dev = b.to("cuda:0")
     ctx = b.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(b))
+    att = pod.PodAttention(pod.config_for_batch(b, wg_per_cu=2))
     try:
         op, od = torch.empty_like(dev.q_prefill), torch.empty_like(dev.q_decode)
         att.hybrid(dev, op, od, ctx)
@@ -154,7 +154,7 @@ def test_four_prompts_beside_long_decodes():
     b = inputs.make_batch(sp, seed=7)
     dev = b.to("cuda:0")
     ctx = b.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(b))
+    att = pod.PodAttention(pod.config_for_batch(b, wg_per_cu=2))
     try:
         op, od = torch.full_like(dev.q_prefill, float("nan")), torch.full_like(dev.q_decode, float("nan"))
         say("four prompts: hybrid_varlen")
