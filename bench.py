@@ -67,10 +67,16 @@ def load_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def time_modes(fns, steps, flush, torch):
+def time_modes(fns, steps, flush, torch, warm=0):
     """Time each callable `steps` times, interleaved round-robin so that every
     mode sees the same clock and thermal conditions; HBM and the caches are
-    flushed (1 GiB write) before every call.  Returns per-mode ms lists."""
+    flushed (1 GiB write) before every call.  `warm` untimed rounds of the
+    same pattern are enqueued right before the timed ones, with no host
+    synchronisation in between.  Returns per-mode ms lists."""
+    for _ in range(warm):
+        for fn in fns:
+            flush.zero_()
+            fn()
     ts = [[] for _ in fns]
     for _ in range(steps):
         for i, fn in enumerate(fns):
@@ -84,12 +90,13 @@ def time_modes(fns, steps, flush, torch):
     return [[a.elapsed_time(b) for a, b in t] for t in ts]
 
 
-def cpu_baseline(batch, seconds_target=12.0):
+def cpu_baseline(batch, seconds_per_run=4.0, runs=3):
     """The fp64 oracle on a bounded sample of the same batch, scaled to one batch.
 
-    A small probe sample sets the pace; the measured sample is then sized to
-    take about `seconds_target` seconds (capped at the whole batch), split
-    between prefill rows and decode requests in proportion to their work."""
+    A small probe sample sets the pace; the sample is then sized to take
+    about `seconds_per_run` seconds (capped at the whole batch), split between
+    prefill rows and decode requests in proportion to their work, run once
+    untimed (warm-up) and `runs` times timed; the median run is scaled."""
     import numpy as np
     import oracle
     w = work_counts(batch)
@@ -122,20 +129,68 @@ def cpu_baseline(batch, seconds_target=12.0):
     rate_p = fr / max(tr, 1e-6)   # oracle FLOP/s on prefill rows
     rate_d = fq / max(tq, 1e-6)
     t_full = w["f_prefill"] / rate_p + w["f_decode"] / rate_d
-    frac = min(1.0, seconds_target / max(t_full, 1e-9))
+    frac = min(1.0, seconds_per_run / max(t_full, 1e-9))
     n_rows = max(1, min(C, int(round(C * frac))))
     n_req = max(1, min(len(lens), int(round(len(lens) * frac))))
-    rows, reqs, f_rows, f_reqs, t_p, t_d = run(n_rows, n_req)
-    # scale each half by its work ratio (visible query-key products)
-    t_batch = t_p * (w["f_prefill"] / f_rows) + t_d * (w["f_decode"] / f_reqs)
+    run(n_rows, n_req)  # warm-up
+    scaled, spent = [], 0.0
+    for _ in range(runs):
+        rows, reqs, f_rows, f_reqs, t_p, t_d = run(n_rows, n_req)
+        # scale each half by its work ratio (visible query-key products)
+        scaled.append(t_p * (w["f_prefill"] / f_rows) + t_d * (w["f_decode"] / f_reqs))
+        spent += t_p + t_d
+    t_batch = statistics.median(scaled)
     try:
         cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     except Exception:
         cores = os.cpu_count() or 1
     return {"value": round(t_batch * 1e6, 1), "unit": "us", "cores": cores, "kind": "oracle",
             "sample": f"{len(rows)} of {C} prefill rows and {len(reqs)} of {len(lens)} decode requests "
-                      f"(all {hq} heads) of the same batch, fp64 C+OpenMP on {cores} threads, "
-                      f"{t_p + t_d:.1f} s measured, scaled by visible query-key products to the whole batch"}
+                      f"(all {hq} heads) of the same batch, fp64 C+OpenMP on {cores} threads of "
+                      f"{cpu_model()}: one warm-up, then the median of {runs} runs ({spent:.1f} s measured), "
+                      f"scaled by visible query-key products to the whole batch",
+            "runs_us": [round(x * 1e6, 1) for x in scaled]}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def environment(torch):
+    """Where the numbers were taken: GPU, ROCm, host CPU and the code."""
+    import hashlib
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    h = hashlib.sha256()
+    for rel in ("bench.py", "include/pod_attn.h") + tuple(
+            os.path.join("prefill_decode_hybrid_amd", "csrc", f) for f in sorted(
+                os.listdir(os.path.join(ROOT, "prefill_decode_hybrid_amd", "csrc")))):
+        try:
+            h.update(open(os.path.join(ROOT, rel), "rb").read())
+        except OSError:
+            pass
+    git = None
+    try:
+        import subprocess
+        git = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except Exception:
+        pass
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_gib": round(props.total_memory / 2**30, 1),
+            "rocm": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "host_cpu": cpu_model(), "host_threads": len(os.sched_getaffinity(0)),
+            "git": git, "source_sha16": h.hexdigest()[:16]}
 
 
 def counters_driver(att, dev, op, od, ctx_host, torch, reps=2):
@@ -169,6 +224,17 @@ def main():
     ap.add_argument("--policy", type=int, default=0, help="fused role policy (enum pod_policy)")
     ap.add_argument("--persistent", action="store_true",
                     help="fused launch as a resident grid looping over the task queues")
+    ap.add_argument("--wg-per-cu", type=int, default=0,
+                    help="resource envelope: 2 or 4 workgroups per CU; 0 chosen per call (default)")
+    ap.add_argument("--slots-x256", type=int, default=0,
+                    help="CU-balanced policy: prefill workgroups kept per CU, in 1/256 (0: the planner's choice)")
+    ap.add_argument("--decode-split-tokens", type=int, default=0,
+                    help="decode tokens per wave task (0: the planner's choice)")
+    ap.add_argument("--prefill-splits", type=int, default=0, help="KV splits per prefill tile (0: the planner's)")
+    ap.add_argument("--split-cap", type=int, default=0,
+                    help="prefill split cap in waves (0: 2; -1: no cap, finest splits)")
+    ap.add_argument("--min-warmup-s", type=float, default=1.0,
+                    help="warm up for at least this many seconds of GPU work before timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this hot path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -190,7 +256,10 @@ def main():
     log(f"[bench] generated in {time.time() - t0:.1f}s: {inputs.describe(batch)}")
     dev = batch.to("cuda:0")
     ctx_host = batch.context_lens.clone().contiguous()
-    att = pod.PodAttention(pod.config_for_batch(batch, policy=args.policy, persistent=int(args.persistent)))
+    knobs = dict(policy=args.policy, persistent=int(args.persistent), wg_per_cu=args.wg_per_cu,
+                 prefill_slots_x256=args.slots_x256, decode_split_tokens=args.decode_split_tokens,
+                 prefill_splits=args.prefill_splits, prefill_split_cap_waves=args.split_cap)
+    att = pod.PodAttention(pod.config_for_batch(batch, **knobs))
     op = torch.empty_like(dev.q_prefill)
     od = torch.empty_like(dev.q_decode)
     op2 = torch.empty_like(dev.q_prefill)
@@ -224,34 +293,47 @@ def main():
         main_s.wait_event(j1)
         main_s.wait_event(j2)
 
-    # untimed check: fusion leaves the result bit-identical to the split launches
+    # untimed check: fusion leaves the result bit-identical to the split
+    # launches of the same resource envelope (a handle fixed to the envelope
+    # the fused plan chose; the timed baselines choose their own)
     fused()
     torch.cuda.synchronize()
     plan = att.stats()
-    serial()
+    same_env = pod.PodAttention(pod.config_for_batch(batch, **dict(knobs, wg_per_cu=plan["wg_per_cu"])))
+    same_env.prefill_only(dev, op2)
+    same_env.decode_only(dev, od2, ctx_host)
     torch.cuda.synchronize()
+    same_env.close()
     same = bool(torch.equal(op, op2) and torch.equal(od, od2))
     finite = bool(torch.isfinite(op.float()).all() and torch.isfinite(od.float()).all())
-    log(f"[bench] plan {plan}; fused==split {same}; finite {finite}")
-
-    for _ in range(args.warmup):
-        fused()
-        if not args.only_hybrid:
-            serial()
-            streams()
+    serial()
     torch.cuda.synchronize()
-
-    host_us = []
-    for _ in range(5):
-        torch.cuda.synchronize()
-        a = time.perf_counter()
-        fused()
-        host_us.append((time.perf_counter() - a) * 1e6)
+    split_plans = {}
+    att.prefill_only(dev, op2)
+    split_plans["prefill_wg_per_cu"] = att.stats()["wg_per_cu"]
+    att.decode_only(dev, od2, ctx_host)
+    split_plans["decode_wg_per_cu"] = att.stats()["wg_per_cu"]
     torch.cuda.synchronize()
+    log(f"[bench] plan {plan}; fused==split {same}; finite {finite}; split calls {split_plans}")
 
+    # Warm-up: every mode once, then the timed loop's own pattern (flush,
+    # fused call) back to back for the requested steps and at least
+    # min_warmup_s, and the timed steps follow with no idle gap.  The GPU runs
+    # the fused kernel measurably slower right after it has idled or after
+    # write-heavy stretches (a fused call behind a 2 ms idle read ~4% slower,
+    # a fused-only loop started after a pause ~3% slower than the same loop
+    # a moment later), so nothing that synchronises with the host may sit
+    # between the warm-up and the timed steps.
+    if not args.only_hybrid:
+        serial()
+        streams()
     torch.cuda.synchronize()
+    (probe,) = time_modes([fused], 2, flush, torch)
+    n_w = max(args.warmup, int(math.ceil(args.min_warmup_s / (max(probe) * 1e-3 + 2e-4))))
+    log(f"[bench] warm-up: {n_w} steps (about {args.min_warmup_s} s), then {args.steps} timed")
+
     wall0 = time.perf_counter()
-    (t_fused,) = time_modes([fused], args.steps, flush, torch)
+    (t_fused,) = time_modes([fused], args.steps, flush, torch, warm=n_w)
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
     t_serial = t_streams = t_fused2 = None
@@ -261,6 +343,15 @@ def main():
         log(f"[bench] serial median {statistics.median(t_serial) * 1e3:.1f} us")
         log(f"[bench] two-stream median {statistics.median(t_streams) * 1e3:.1f} us")
     log(f"[bench] fused median {statistics.median(t_fused) * 1e3:.1f} us")
+
+    # host-side cost of one call (planning and launch), measured last
+    host_us = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        fused()
+        host_us.append((time.perf_counter() - a) * 1e6)
+    torch.cuda.synchronize()
 
     w = work_counts(batch)
     med = statistics.median(t_fused) * 1e-3  # seconds
@@ -315,12 +406,16 @@ def main():
         "speedup_vs_serial": round(statistics.median(t_serial) / statistics.median(t_fused2), 4) if t_serial else None,
         "speedup_vs_two_stream": round(statistics.median(t_streams) / statistics.median(t_fused2), 4) if t_streams else None,
         "host_call_us": round(statistics.median(host_us), 1),
-        "wall_ms_per_step_incl_flush": round((wall1 - wall0) * 1e3 / args.steps, 4),
+        "warmup_steps_run": n_w,
+        "wall_ms_per_step_incl_flush_and_warmup": round((wall1 - wall0) * 1e3 / (args.steps + n_w), 4),
         "fused_equals_split": same,
         "finite": finite,
         "plan": plan,
+        "split_calls": split_plans,
         "gpu": torch.cuda.get_device_name(0),
+        "environment": environment(torch),
         "kernel_code": kernel_code_hash(),
+        "knobs": knobs,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")

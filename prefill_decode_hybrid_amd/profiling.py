@@ -156,6 +156,11 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
 
 SIMDS = 256 * 4       # MI355X: 256 compute units of 4 SIMDs
 CLOCK_HZ = 2.4e9      # peak engine clock
+# Achieved occupancy: SQ_WAVE_CYCLES / SQ_BUSY_CYCLES is proportional to the
+# waves resident per compute unit; the factor is read off a dispatch of known
+# occupancy (a decode launch of exactly one 4-wave workgroup on each of the
+# 256 CUs reads 7.3, i.e. ~2 per resident wave, so per SIMD divide by 2 * 4).
+OCC_NORM = 8.0
 RATIOS = [  # (label, numerator, denominator): definitions that need no per-chip normalisation
     ("vector instructions per MFMA", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
     ("exp/transcendental instructions per MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA"),
@@ -206,6 +211,13 @@ def counters_main(argv):
             k = short_name(r["Kernel_Name"])
             if k in mean:
                 dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    cells = []
+    for k in kernels:
+        m = mean[k]
+        ok = "SQ_WAVE_CYCLES" in m and m.get("SQ_BUSY_CYCLES")
+        cells.append(f"{m['SQ_WAVE_CYCLES'] / m['SQ_BUSY_CYCLES'] / OCC_NORM:.2f}" if ok else "")
+    if any(cells):
+        lines.append("| resident waves per SIMD (achieved occupancy) | " + " | ".join(cells) + " |")
     if dur:
         lines.append("| mean duration in these runs (us) | " +
                      " | ".join(f"{statistics.mean(dur[k]):.1f}" if dur[k] else "" for k in kernels) + " |")
@@ -236,7 +248,7 @@ def main():
     dur = kernel_durations(a.trace)
     tr = traffic(a.fetch, a.write)
     src = kernel_code_hash()
-    hybrid = next((k for k in tr["kernels"] if k.startswith("pod_hybrid_kernel")), None)
+    hybrid = next((k for k in tr["kernels"] if k.startswith("pod_hybrid")), None)
     rec = {"workload": a.workload, "kernel_code": src, "kernel": hybrid,
            "hbm_bytes_per_launch": tr["kernels"][hybrid]["hbm_bytes"] if hybrid else None,
            "calibration": {"copy_bytes": CALIB_BYTES, "fetch_bytes_per_kib": tr["fetch_bytes_per_kib"],
@@ -247,15 +259,16 @@ def main():
     lines = [f"# rocprofv3 summary: {a.workload}", "", f"kernel code objects: `{src}`", ""]
     if a.command:
         lines += ["Commands:", "", "```", a.command, "```", ""]
-    lines += ["| kernel | calls | mean us | median us | min us | HBM read MB | HBM write MB |",
-              "|---|---|---|---|---|---|---|"]
+    lines += ["| kernel | calls | mean us | median us | min us | HBM read MB | HBM write MB | HBM GB/s (mean) |",
+              "|---|---|---|---|---|---|---|---|"]
     for k, v in sorted(dur.items(), key=lambda kv: -kv[1]["mean_us"]):
         if not k.startswith("pod_"):
             continue
         t = tr["kernels"].get(k, {})
         rd = f"{t['hbm_read_bytes'] / 1e6:.1f}" if t else ""
         wr = f"{t['hbm_write_bytes'] / 1e6:.1f}" if t else ""
-        lines.append(f"| `{k}` | {v['calls']} | {v['mean_us']:.1f} | {v['median_us']:.1f} | {v['min_us']:.1f} | {rd} | {wr} |")
+        bw = f"{t['hbm_bytes'] / (v['mean_us'] * 1e-6) / 1e9:.0f}" if t else ""
+        lines.append(f"| `{k}` | {v['calls']} | {v['mean_us']:.1f} | {v['median_us']:.1f} | {v['min_us']:.1f} | {rd} | {wr} | {bw} |")
     lines += ["", f"Counter calibration: a {CALIB_BYTES >> 20} MiB device copy reads "
               f"{CALIB_BYTES / tr['fetch_bytes_per_kib'] :.0f} KiB of FETCH_SIZE and writes "
               f"{CALIB_BYTES / tr['write_bytes_per_kib']:.0f} KiB of WRITE_SIZE, so one FETCH_SIZE KiB is "
