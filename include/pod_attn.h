@@ -138,7 +138,25 @@ typedef struct {
                                  task; same tasks and results.  0: one per task       */
     int32_t prefill_splits;     /* KV splits per prefill tile (at most one per minimum
                                  split); 0 selects the planner's choice above        */
+    int32_t record_roles;       /* 1: fused launches write one pod_attn_task_record per
+                                 task (read with pod_attn_role_trace); 0: none        */
 } pod_attn_config;
+
+/* One task of a fused launch as it ran: the virtual-workgroup mix the
+ * Silicon & Systems digest asks the runtime to report ("Isolation and
+ * predictability").  cu_key = XCC << 8 | shader engine << 5 | shader array
+ * << 4 | CU of the compute unit the workgroup ran on; role 0 prefill, 1
+ * decode; task its index in that role's list; start and end read from the
+ * chip-wide 100 MHz real-time counter when the workgroup began the task and
+ * when all its waves were done with it. */
+typedef struct {
+    uint32_t cu_key;
+    int32_t role;
+    int32_t task;
+    int32_t reserved;
+    uint64_t start;
+    uint64_t end;
+} pod_attn_task_record;
 
 typedef struct {
     const void *q;              /* device [chunk_len, Hq, head_dim]                    */
@@ -236,7 +254,8 @@ int pod_attn_hybrid(pod_attn_handle *h, const void *k_pool, const void *v_pool, 
  * earlier call left there), then the fused launch; outputs are bit for bit
  * those of pod_attn_hybrid on the same batch and config.  A batch whose
  * workspace (counters, prefill-split and decode-split partials) exceeds the
- * scratch returns POD_ERR_WORKSPACE before anything is enqueued; other
+ * scratch returns POD_ERR_WORKSPACE before anything is enqueued, and a
+ * config with record_roles = 1 POD_ERR_UNSUPPORTED (no trace region); other
  * errors as for pod_attn_create and pod_attn_hybrid (a HIP failure is
  * POD_ERR_HIP; there is no handle, so no error text and no stats).  All
  * calls on one GPU share its scratch: calls that overlap in time on one GPU
@@ -268,6 +287,14 @@ int pod_attn_prefill_only_varlen(pod_attn_handle *h, const void *k_pool, const v
 int pod_attn_plan_varlen(const pod_attn_config *cfg, int32_t num_cus, int32_t mode,
                          const pod_prefill_batch *prefill, const pod_decode_args *decode,
                          pod_attn_stats *out);
+
+/* Role trace of the last fused call (pod_attn_hybrid or _varlen) made by a
+ * handle created with record_roles = 1: waits for the device, then copies up
+ * to `capacity` records into `out` (host memory, prefill tasks first, then
+ * decode workgroup tasks) and sets *count to the number the launch wrote
+ * (0 if no fused call recorded yet).  POD_ERR_INVALID_ARG if the handle does
+ * not record roles.  A diagnostic call: it synchronises the device. */
+int pod_attn_role_trace(pod_attn_handle *h, pod_attn_task_record *out, int32_t capacity, int32_t *count);
 
 /* Copy the plan of the last successful compute call into *out. */
 int pod_attn_get_stats(const pod_attn_handle *h, pod_attn_stats *out);

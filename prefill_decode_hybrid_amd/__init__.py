@@ -27,7 +27,7 @@ POD_MAX_CHUNKS = 64
 
 EXPORTED = ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_prefill_only",
             "pod_attn_decode_only", "pod_attn_hybrid_noalloc", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
-            "pod_attn_get_stats", "pod_attn_plan", "pod_attn_plan_varlen",
+            "pod_attn_get_stats", "pod_attn_role_trace", "pod_attn_plan", "pod_attn_plan_varlen",
             "pod_attn_status_string", "pod_attn_last_error")
 
 
@@ -40,7 +40,13 @@ class PodAttnConfig(ctypes.Structure):
                 ("wg_per_cu", ctypes.c_int32), ("prefill_split_cap_waves", ctypes.c_int32),
                 ("policy", ctypes.c_int32), ("device", ctypes.c_int32),
                 ("prefill_slots_x256", ctypes.c_int32), ("decode_split_tokens", ctypes.c_int32),
-                ("persistent", ctypes.c_int32), ("prefill_splits", ctypes.c_int32)]
+                ("persistent", ctypes.c_int32), ("prefill_splits", ctypes.c_int32),
+                ("record_roles", ctypes.c_int32)]
+
+
+class PodTaskRecord(ctypes.Structure):
+    _fields_ = [("cu_key", ctypes.c_uint32), ("role", ctypes.c_int32), ("task", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("start", ctypes.c_uint64), ("end", ctypes.c_uint64)]
 
 
 class PodPrefillArgs(ctypes.Structure):
@@ -104,6 +110,7 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_plan_varlen.argtypes = [ctypes.POINTER(PodAttnConfig), i32, i32, ctypes.POINTER(PodPrefillBatch),
                                          ctypes.POINTER(PodDecodeArgs), ctypes.POINTER(PodAttnStats)]
     lib.pod_attn_get_stats.argtypes = [P, ctypes.POINTER(PodAttnStats)]
+    lib.pod_attn_role_trace.argtypes = [P, ctypes.POINTER(PodTaskRecord), i32, ctypes.POINTER(i32)]
     lib.pod_attn_plan.argtypes = [ctypes.POINTER(PodAttnConfig), i32, i32, ctypes.POINTER(PodPrefillArgs),
                                   ctypes.POINTER(PodDecodeArgs), ctypes.POINTER(PodAttnStats)]
     lib.pod_attn_status_string.argtypes = [ctypes.c_int]
@@ -113,7 +120,7 @@ def load(path: str = LIB_PATH):
     for name in ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_hybrid_noalloc",
                  "pod_attn_prefill_only",
                  "pod_attn_decode_only", "pod_attn_hybrid_noalloc", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
-                 "pod_attn_get_stats", "pod_attn_plan", "pod_attn_plan_varlen"):
+                 "pod_attn_get_stats", "pod_attn_role_trace", "pod_attn_plan", "pod_attn_plan_varlen"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -130,11 +137,11 @@ def make_config(dtype=POD_BF16, num_q_heads=32, num_kv_heads=8, head_dim=128, pa
                 sm_scale=0.0, max_chunk_len=4096, max_num_decode=256, max_context=32768,
                 max_total_context=0, wg_per_cu=0, prefill_split_cap_waves=0,
                 policy=POD_POLICY_CU_BALANCED, device=-1, prefill_slots_x256=0,
-                decode_split_tokens=0, persistent=0, prefill_splits=0) -> PodAttnConfig:
+                decode_split_tokens=0, persistent=0, prefill_splits=0, record_roles=0) -> PodAttnConfig:
     return PodAttnConfig(dtype, num_q_heads, num_kv_heads, head_dim, page_size, sm_scale,
                          max_chunk_len, max_num_decode, max_context, max_total_context,
                          wg_per_cu, prefill_split_cap_waves, policy, device, prefill_slots_x256,
-                         decode_split_tokens, persistent, prefill_splits)
+                         decode_split_tokens, persistent, prefill_splits, record_roles)
 
 
 def _ptr(t) -> Optional[int]:
@@ -242,6 +249,18 @@ def pod_attn_get_stats(h) -> dict:
     return st.as_dict()
 
 
+def pod_attn_role_trace(h) -> list:
+    """Task records of the last fused call of a recording handle:
+    [(cu_key, role, task, start, end)], start/end in 100 MHz ticks."""
+    lib = load()
+    count = ctypes.c_int32(0)
+    _check(h, lib.pod_attn_role_trace(h, None, 0, ctypes.byref(count)), "pod_attn_role_trace")
+    n = count.value
+    recs = (PodTaskRecord * max(1, n))()
+    _check(h, lib.pod_attn_role_trace(h, recs, n, ctypes.byref(count)), "pod_attn_role_trace")
+    return [(r.cu_key, r.role, r.task, r.start, r.end) for r in recs[:n]]
+
+
 def pod_attn_plan(cfg: PodAttnConfig, num_cus: int, mode: int, prefill=None, decode=None) -> dict:
     """Host-only plan (no GPU needed).  Raises PodAttnError on invalid arguments."""
     st = PodAttnStats()
@@ -317,6 +336,9 @@ class PodAttention:
 
     def stats(self) -> dict:
         return pod_attn_get_stats(self.h)
+
+    def role_trace(self) -> list:
+        return pod_attn_role_trace(self.h)
 
 
 def config_for_batch(batch, **kw) -> PodAttnConfig:

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -22,6 +23,7 @@ struct pod_attn_handle {
   char* ws = nullptr;
   pod::WorkspaceLayout lay;
   pod_attn_stats stats{};
+  int64_t traced_tasks = 0;  // records of the last fused launch that recorded its roles
   char err[256] = {0};
 };
 
@@ -51,6 +53,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   if (c->prefill_splits < 0) return POD_ERR_INVALID_ARG;
   if (c->policy < pod::kPolicyCuBalanced || c->policy > pod::kPolicyStatic) return POD_ERR_INVALID_ARG;
   if (c->prefill_slots_x256 < 0 || c->prefill_slots_x256 > 4 * 256) return POD_ERR_INVALID_ARG;
+  if (c->record_roles != 0 && c->record_roles != 1) return POD_ERR_INVALID_ARG;
   if (c->decode_split_tokens != 0 &&
       (c->decode_split_tokens % pod::kPageSize != 0 ||
        c->decode_split_tokens < pod::min_split_tokens(s.dtype, c->max_context) ||
@@ -63,6 +66,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   lim.wg_per_cu = c->persistent ? 2 : c->wg_per_cu;
   lim.cap_waves = c->prefill_split_cap_waves ? c->prefill_split_cap_waves : 2;
   lim.prefill_splits = c->prefill_splits;
+  lim.record_roles = c->record_roles != 0;
   lim.policy = c->policy;
   lim.slots_x256 = c->prefill_slots_x256;
   lim.split_tokens = c->decode_split_tokens;
@@ -175,6 +179,7 @@ void fill_params(const pod::Shape& s, float sm_scale, char* ws, const pod::Works
   p.d_cnt = reinterpret_cast<uint32_t*>(ws + lay.d_cnt);
   p.p_part = reinterpret_cast<float*>(ws + lay.p_part);
   p.d_part = reinterpret_cast<float*>(ws + lay.d_part);
+  p.trace = lay.trace_bytes ? ws + lay.trace : nullptr;
   if (pl.has_p) {
     p.qp = pv.q;
     p.op = pv.o;
@@ -238,6 +243,7 @@ int run(pod_attn_handle* h, int mode, const void* k_pool, const void* v_pool, in
     if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
   }
   fill_stats(pl, &h->stats);
+  if (p.trace && kernel_of(pl) == pod::kKernelHybrid) h->traced_tasks = (int64_t)pl.p_tasks + pl.d_wg_tasks;
   return POD_OK;
 }
 
@@ -339,6 +345,7 @@ int pod_attn_hybrid_noalloc(const pod_attn_config* cfg, const void* k_pool, cons
   if (!pod::have_kernel(s.dtype, s.d, s.G)) return POD_ERR_UNSUPPORTED;
   rc = check_decode(decode);
   if (rc) return rc;
+  if (lim.record_roles) return POD_ERR_UNSUPPORTED;  // no trace region in the fixed scratch
   PrefillView pv;
   rc = prefill_one(prefill, pv);
   if (rc) return rc;
@@ -397,6 +404,19 @@ int pod_attn_prefill_only_varlen(pod_attn_handle* h, const void* k_pool, const v
   PrefillView pv;
   const int rc = prefill_many(prefill, pv);
   return rc ? rc : run(h, pod::kModePrefill, k_pool, v_pool, num_pages, pv, nullptr, stream);
+}
+
+int pod_attn_role_trace(pod_attn_handle* h, pod_attn_task_record* out, int32_t capacity, int32_t* count) {
+  if (!h || !count || capacity < 0 || (capacity > 0 && !out)) return POD_ERR_INVALID_ARG;
+  if (!h->lay.trace_bytes) return POD_ERR_INVALID_ARG;  // the handle does not record roles
+  static_assert(sizeof(pod_attn_task_record) == pod::kTraceRecordBytes, "trace record layout");
+  *count = (int32_t)h->traced_tasks;
+  const int64_t n = std::min<int64_t>(capacity, h->traced_tasks);
+  if (n <= 0) return POD_OK;
+  hipError_t e = hipSetDevice(h->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(out, h->ws + h->lay.trace, (size_t)n * sizeof(pod_attn_task_record), hipMemcpyDeviceToHost);
+  return e == hipSuccess ? POD_OK : hip_fail(h, e, "role trace copy");
 }
 
 int pod_attn_get_stats(const pod_attn_handle* h, pod_attn_stats* out) {

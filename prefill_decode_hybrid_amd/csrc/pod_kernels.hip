@@ -2043,6 +2043,19 @@ DEV bool ticket_policy(const PodParams& p) {
 // A CU-balanced launch resident in one round (fixed_order) also hands out
 // roles by workgroup id -- one role's tasks first, then the other's -- with
 // no atomics in front of the work.
+// Role trace: one 32-byte record per task of a fused launch (the realised
+// mix of virtual workgroups, which the Silicon & Systems digest asks the
+// runtime to report): the key of the CU it ran on, its role and task, and
+// its start and end on the chip-wide 100 MHz real-time counter.  Written by
+// thread 0 with plain vector stores once the task is done.
+DEV void trace_task(const PodParams& p, int role, int task, uint32_t key, uint64_t t0) {
+  const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+  const int slot = role == 0 ? task : p.p_tasks + task;
+  uint4* r = reinterpret_cast<uint4*>(p.trace + (int64_t)slot * 32);
+  r[0] = make_uint4(key, (uint32_t)role, (uint32_t)task, 0u);
+  r[1] = make_uint4((uint32_t)t0, (uint32_t)(t0 >> 32), (uint32_t)t1, (uint32_t)(t1 >> 32));
+}
+
 template <class RunP, class RunD>
 DEV void fused_body(const PodParams& p, RunP&& run_prefill, RunD&& run_decode) {
   __shared__ int role_task[4];
@@ -2063,6 +2076,7 @@ DEV void fused_body(const PodParams& p, RunP&& run_prefill, RunD&& run_decode) {
       pick_and_claim(p, role, task, counted, key);
       last = leave_claims(p);  // one claim per workgroup
     }
+    if (p.trace && !key) key = cu_key();
     cu_word = key;
     role_task[0] = role;
     role_task[1] = task;
@@ -2070,16 +2084,27 @@ DEV void fused_body(const PodParams& p, RunP&& run_prefill, RunD&& run_decode) {
     role_task[3] = last;
   }
   __syncthreads();
+  const uint64_t t0 = p.trace ? __builtin_amdgcn_s_memrealtime() : 0;
   const int role = role_task[0], task = role_task[1];
   if (role_task[3] && ticket_policy(p)) clear_tickets(p);
+  bool ran = false;
   if (role == 0) {
-    if (task < p.p_tasks) run_prefill(task);
+    if (task < p.p_tasks) {
+      run_prefill(task);
+      ran = true;
+    }
   } else {
-    if (task < p.d_wg_tasks) run_decode(task);
+    if (task < p.d_wg_tasks) {
+      run_decode(task);
+      ran = true;
+    }
   }
-  if (role_task[2]) {
+  if (role_task[2] || p.trace) {
     __syncthreads();
-    if (threadIdx.x == 0) atomicSub(p.tickets + cu_word, role == 0 ? 1u : 0x10000u);
+    if (threadIdx.x == 0) {
+      if (role_task[2]) atomicSub(p.tickets + cu_word, role == 0 ? 1u : 0x10000u);
+      if (p.trace && ran) trace_task(p, role, task, cu_word, t0);
+    }
   }
 }
 
@@ -2146,6 +2171,7 @@ __global__ __launch_bounds__(256, 2) void pod_persistent_kernel(PodParams p) {
       role_task[3] = last;
     }
     __syncthreads();
+    const uint64_t t0 = p.trace ? __builtin_amdgcn_s_memrealtime() : 0;
     const int role = role_task[0], task = role_task[1];
     if (role_task[3] && ticket_policy(p)) clear_tickets(p);
     if (role == 0) {
@@ -2157,6 +2183,7 @@ __global__ __launch_bounds__(256, 2) void pod_persistent_kernel(PodParams p) {
     }
     __syncthreads();  // the task's LDS and role_task are free again
     if (threadIdx.x == 0 && role_task[2]) atomicSub(p.tickets + cu_word, role == 0 ? 1u : 0x10000u);
+    if (threadIdx.x == 0 && p.trace) trace_task(p, role, task, cu_word ? cu_word : cu_key(), t0);
   }
 }
 

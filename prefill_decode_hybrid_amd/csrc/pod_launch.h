@@ -54,6 +54,9 @@ struct PodParams {
   int share_num, share_den, cu_prefill_x256, policy, grid;
   int fixed_order;   // fused launch: 1 / 2 = the first workgroup ids run the prefill / decode tasks
   int prefill_priority;  // 1: prefill waves issue above decode waves (s_setprio)
+  // role trace (fused launches): task t's record at trace + 32 * (prefill t,
+  // or p_tasks + decode workgroup task t); nullptr when not recording
+  char* trace;
 };
 
 // The parameter block is the kernels' only argument (kernel arguments are

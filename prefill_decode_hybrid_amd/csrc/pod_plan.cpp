@@ -84,6 +84,11 @@ WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim) {
   const int G = s.hq / s.hkv;
   const size_t rec = ((size_t)G * (s.d + 2) + 3) & ~size_t(3);  // 16-byte records
   at = align(at + (size_t)std::max<int64_t>(1, lim.cap_wave_tasks) * rec * 4);
+  w.trace = at;
+  if (lim.record_roles)
+    w.trace_bytes = (size_t)(lim.cap_prefill_tasks + (lim.cap_wave_tasks + kWavesPerWG - 1) / kWavesPerWG + 1) *
+                    kTraceRecordBytes;
+  at = align(at + w.trace_bytes);
   w.total = at;
   return w;
 }

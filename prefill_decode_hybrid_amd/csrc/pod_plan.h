@@ -75,6 +75,7 @@ struct Limits {
   int slots_x256 = 0;  // prefill slots per CU for the CU-balanced policy; 0: from the batch
   int split_tokens = 0;  // decode tokens per wave task; 0: from the batch
   bool persistent = false;  // fused launch as a resident grid looping over the queues
+  bool record_roles = false;  // fused launches write one record per task (role trace)
   int num_cus = 0;
   // capacities derived by derive_capacities()
   int64_t cap_prefill_tasks = 0, cap_wave_tasks = 0, cap_tiles = 0;
@@ -145,8 +146,10 @@ int check_shape(const Shape& s);
 void derive_capacities(const Shape& s, Limits& lim);
 
 struct WorkspaceLayout {
-  size_t ctrl = 0, tickets = 0, p_cnt = 0, d_cnt = 0, p_part = 0, d_part = 0, total = 0;
+  size_t ctrl = 0, tickets = 0, p_cnt = 0, d_cnt = 0, p_part = 0, d_part = 0, trace = 0, total = 0;
+  size_t trace_bytes = 0;  // role-trace records (0 when not recording)
 };
+constexpr int kTraceRecordBytes = 32;  // cu key, role, task, pad, start and end times
 WorkspaceLayout workspace_layout(const Shape& s, const Limits& lim);
 // The workspace one planned call uses (counters and partials for exactly its tasks).
 WorkspaceLayout workspace_layout_for_plan(const Shape& s, const Plan& pl);
