@@ -230,6 +230,8 @@ def main():
                     help="CU-balanced policy: prefill workgroups kept per CU, in 1/256 (0: the planner's choice)")
     ap.add_argument("--decode-split-tokens", type=int, default=0,
                     help="decode tokens per wave task (0: the planner's choice)")
+    ap.add_argument("--decode-tail-split-tokens", type=int, default=0,
+                    help="cut each decode request's tail into splits of this many tokens (0: none)")
     ap.add_argument("--prefill-splits", type=int, default=0, help="KV splits per prefill tile (0: the planner's)")
     ap.add_argument("--split-cap", type=int, default=0,
                     help="prefill split cap in waves (0: 2; -1: no cap, finest splits)")
@@ -258,7 +260,8 @@ def main():
     ctx_host = batch.context_lens.clone().contiguous()
     knobs = dict(policy=args.policy, persistent=int(args.persistent), wg_per_cu=args.wg_per_cu,
                  prefill_slots_x256=args.slots_x256, decode_split_tokens=args.decode_split_tokens,
-                 prefill_splits=args.prefill_splits, prefill_split_cap_waves=args.split_cap)
+                 prefill_splits=args.prefill_splits, prefill_split_cap_waves=args.split_cap,
+                 decode_tail_split_tokens=args.decode_tail_split_tokens)
     att = pod.PodAttention(pod.config_for_batch(batch, **knobs))
     op = torch.empty_like(dev.q_prefill)
     od = torch.empty_like(dev.q_decode)

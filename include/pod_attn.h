@@ -140,6 +140,14 @@ typedef struct {
                                  split); 0 selects the planner's choice above        */
     int32_t record_roles;       /* 1: fused launches write one pod_attn_task_record per
                                  task (read with pod_attn_role_trace); 0: none        */
+    int32_t decode_tail_split_tokens; /* > 0: the tail of every decode request (its
+                                 last full split and the remainder) is cut into splits
+                                 of this many tokens, numbered after every other split
+                                 so a launch's last decode tasks are short: a multiple
+                                 of 16, at least the decode split minimum above; not
+                                 below the decode split means no tail splits.  0: no
+                                 tail splits (the planner's choice: measured faster
+                                 on every batch but the prefill-heavy one)            */
 } pod_attn_config;
 
 /* One task of a fused launch as it ran: the virtual-workgroup mix the
@@ -226,6 +234,8 @@ typedef struct {
     int32_t prefill_priority;   /* 1: prefill waves issued above co-resident decode
                                    waves; 0: equal (a decode-first launch whose
                                    workgroups all start in the first round)         */
+    int32_t decode_tail_split_tokens; /* tokens per tail split of a decode request;
+                                   0 when the tail is one split                      */
 } pod_attn_stats;
 
 /* Validate `cfg`, pick the device, reserve the workspace.  Returns POD_OK and

@@ -59,6 +59,12 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
        c->decode_split_tokens < pod::min_split_tokens(s.dtype, c->max_context) ||
        c->decode_split_tokens > pod::kMaxSplitTokens))
     return POD_ERR_INVALID_ARG;
+  if (c->decode_tail_split_tokens < 0 ||
+      (c->decode_tail_split_tokens > 0 &&
+       (c->decode_tail_split_tokens % pod::kPageSize != 0 ||
+        c->decode_tail_split_tokens < pod::min_split_tokens(s.dtype, c->max_context) ||
+        c->decode_tail_split_tokens > pod::kMaxSplitTokens)))
+    return POD_ERR_INVALID_ARG;
   lim.max_chunk_len = c->max_chunk_len;
   lim.max_num_decode = c->max_num_decode;
   lim.max_context = c->max_context;
@@ -70,6 +76,7 @@ int validate_config(const pod_attn_config* c, pod::Shape& s, pod::Limits& lim, f
   lim.policy = c->policy;
   lim.slots_x256 = c->prefill_slots_x256;
   lim.split_tokens = c->decode_split_tokens;
+  lim.tail_split_tokens = c->decode_tail_split_tokens;
   lim.persistent = c->persistent != 0;
   scale = c->sm_scale > 0.0f ? c->sm_scale : 1.0f / std::sqrt((float)s.d);
   return POD_OK;
@@ -93,6 +100,7 @@ void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
   st->prefill_split_keys = pl.has_p ? pl.ch[0].split_keys : 0;
   st->prefill_tasks = pl.has_p ? pl.p_tasks : 0;
   st->decode_split_tokens = pl.T;
+  st->decode_tail_split_tokens = pl.has_d && pl.tail_k ? pl.T2 : 0;
   st->decode_wave_tasks = pl.has_d ? pl.d_wave_tasks : 0;
   st->decode_wg_tasks = pl.has_d ? pl.d_wg_tasks : 0;
   st->share_num = pl.share_num;
@@ -203,9 +211,11 @@ void fill_params(const pod::Shape& s, float sm_scale, char* ws, const pod::Works
     p.stride = da->page_table_stride;
     p.N = pl.N;
     p.T = pl.T;
+    p.T2 = pl.T2;
+    p.tail_k = pl.tail_k;
     p.d_wave_tasks = pl.d_wave_tasks;
     p.d_units = pl.d_wave_tasks / s.hkv;
-    p.d_full = pl.d_full;
+    p.d_long = pl.d_long;
     p.ctx_cap = pl.d_max;
     p.d_wg_tasks = pl.d_wg_tasks;
   }

@@ -343,14 +343,14 @@ struct DecFrag {
 // the host copy the launch was planned from) is dropped instead of written.
 DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S, int& base) {
   const int lane = lane_id();
-  const bool rem = unit >= p.d_full;
-  const uint32_t u = (uint32_t)(rem ? unit - p.d_full : unit);
+  const bool sp = unit >= p.d_long;
+  const uint32_t u = (uint32_t)(sp ? unit - p.d_long : unit);
   uint32_t key_acc = 0, base_acc = 0;
   for (int c0 = 0; c0 < p.N; c0 += kUnitScanLanes) {
     const int idx = c0 + lane;
     int L = idx < p.N ? min(p.ctx[idx], p.ctx_cap) : 0;
     L = max(L, 0);
-    const uint32_t own = unit_pack(L, p.T, rem);
+    const uint32_t own = unit_pack(L, p.T, p.T2, p.tail_k, sp);
     uint32_t incl = own;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -362,7 +362,7 @@ DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S, int& 
       const uint64_t hit = __ballot(key_acc + unit_phase(incl) > u);
       const int first = __builtin_ctzll(hit);
       r = c0 + first;
-      unit_select(u, rem, key_acc, base_acc, __shfl(own, first, 64), __shfl(incl, first, 64), s, S, base);
+      unit_select(u, sp, key_acc, base_acc, __shfl(own, first, 64), __shfl(incl, first, 64), s, S, base);
       return base >= 0 && base + S <= p.d_units;
     }
     key_acc += unit_phase(total);
@@ -418,8 +418,8 @@ DEV void decode_wave(const PodParams& p, int wt, float* wl) {
   S = __builtin_amdgcn_readfirstlane(S);
   base = __builtin_amdgcn_readfirstlane(base);
   const int L = min(p.ctx[r], p.ctx_cap);
-  const int t0 = s * p.T;
-  const int t1 = min(t0 + p.T, L);
+  int t0, t1;
+  unit_range(L, p.T, p.T2, p.tail_k, s, t0, t1);
   const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
   const int slot = lane >> 4, j = lane & 15;
 
@@ -651,8 +651,8 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   S = __builtin_amdgcn_readfirstlane(S);
   base = __builtin_amdgcn_readfirstlane(base);
   const int L = min(p.ctx[r], p.ctx_cap);
-  const int t0 = s * p.T;
-  const int t1 = min(t0 + p.T, L);
+  int t0, t1;
+  unit_range(L, p.T, p.T2, p.tail_k, s, t0, t1);
   const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
   const int npair = (npg + 1) >> 1;
   const int kk = lane & 15, q4 = lane >> 4;       // MFMA roles: key / head column, quad
@@ -668,11 +668,14 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
     pid[k] = (int)min((uint32_t)v, p.num_pages - 1u);
   }
   auto page_id = [&](int i) __attribute__((always_inline)) {
+    // a select over the id registers (no branch: it sits between loads)
     const int l = i & 63, k = i >> 6;
     int v = __builtin_amdgcn_readlane(pid[0], l);
 #pragma unroll
-    for (int j = 1; j < kSplitIdRegs; ++j)
-      if (k == j) v = __builtin_amdgcn_readlane(pid[j], l);
+    for (int j = 1; j < kSplitIdRegs; ++j) {
+      const int w = __builtin_amdgcn_readlane(pid[j], l);
+      v = k == j ? w : v;
+    }
     return v;
   };
 
@@ -689,11 +692,13 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
       qf[c] = as_bf16x8(v);
     }
   }
-  const int64_t tok_bytes = (int64_t)hkv * D * 2;
-  const int64_t page_bytes = kPageSize * tok_bytes;
-  const int64_t lane_off = (int64_t)lrow * tok_bytes + (int64_t)g * C::ROWB + lchk * 16;
-  const char* kb = reinterpret_cast<const char*>(p.k_pool) + lane_off;
-  const char* vb = reinterpret_cast<const char*>(p.v_pool) + lane_off;
+  // Loads are buffer loads on a descriptor of the page (a scalar base and a
+  // 32-bit lane offset inside the page).  A page past the split's last gets
+  // an empty descriptor: its loads return zeros without touching memory, so
+  // every pair issues the same loads and the waits count them statically.
+  const uint32_t tok_bytes = (uint32_t)hkv * D * 2;
+  const uint32_t page_bytes = kPageSize * tok_bytes;
+  const uint32_t lane_off = (uint32_t)lrow * tok_bytes + (uint32_t)g * C::ROWB + lchk * 16;
   char* kl = lds;            // K rows of the pair
   char* vl = lds + C::OPB;   // V rows of the pair
 
@@ -703,35 +708,65 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   float m = kNegInf, l = 0.0f;
 
   u32x4_t kr[2][2][NI], vr[2][2][NI];
-  // A missing second page (odd page count) re-reads the last page; every key
-  // past t1 is masked in consume(), so its values never reach the result.
+  // Keys past t1 (the rest of the last page, a missing second page) are
+  // masked in compute(), so their values never reach the result.
   auto issue = [&](u32x4_t (&kd)[2][NI], u32x4_t (&vd)[2][NI], int pair) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-      const int pg = min(2 * pair + pp, npg - 1);
-      const int64_t off = (int64_t)page_id(pg) * page_bytes;
+      const int pg = 2 * pair + pp;
+      const int64_t off = (int64_t)page_id(min(pg, npg - 1)) * page_bytes;
+      const int nrec = pg < npg ? (int)page_bytes : 0;
+      const Rsrc rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(p.k_pool) + off), (short)0, nrec, 0x00020000);
+      const Rsrc rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(p.v_pool) + off), (short)0, nrec, 0x00020000);
 #pragma unroll
       for (int u = 0; u < NI; ++u)
-        kd[pp][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + off + u * C::RPI * tok_bytes));
+        kd[pp][u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(lane_off + u * C::RPI * tok_bytes), 0, kNonTemporal);
 #pragma unroll
       for (int u = 0; u < NI; ++u)
-        vd[pp][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + off + u * C::RPI * tok_bytes));
+        vd[pp][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(lane_off + u * C::RPI * tok_bytes), 0, kNonTemporal);
     }
   };
 
-  auto consume = [&](const u32x4_t (&kd)[2][NI], const u32x4_t (&vd)[2][NI], int pair) __attribute__((always_inline)) {
+  // K and V rows of a pair -> LDS; the registers are free for the next
+  // loads once this is issued.  Only a pair that reaches past the split's
+  // last key (uniform test) zeroes its invisible V rows.
+  auto stage = [&](const u32x4_t (&kd)[2][NI], const u32x4_t (&vd)[2][NI], int pair) __attribute__((always_inline)) {
     const int kbase = t0 + 32 * pair;
-    // K and V rows of the pair -> LDS (invisible V rows zeroed)
+    const bool full = kbase + 32 <= t1;
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
         const int row = 16 * pp + u * C::RPI + lrow;
-        const bool ok = kbase + row < t1;
         *reinterpret_cast<u32x4_t*>(kl + row * C::ROWB + ((lchk ^ ksw_rows<C::CHR>(row)) << 4)) = kd[pp][u];
-        *reinterpret_cast<u32x4_t*>(vl + row * C::ROWB + ((lchk ^ vsw_decode<C::CHR>(row)) << 4)) =
-            ok ? vd[pp][u] : (u32x4_t){0u, 0u, 0u, 0u};
       }
+    if (full) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+          const int row = 16 * pp + u * C::RPI + lrow;
+          *reinterpret_cast<u32x4_t*>(vl + row * C::ROWB + ((lchk ^ vsw_decode<C::CHR>(row)) << 4)) = vd[pp][u];
+        }
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+          const int row = 16 * pp + u * C::RPI + lrow;
+          const bool ok = kbase + row < t1;
+          *reinterpret_cast<u32x4_t*>(vl + row * C::ROWB + ((lchk ^ vsw_decode<C::CHR>(row)) << 4)) =
+              ok ? vd[pp][u] : (u32x4_t){0u, 0u, 0u, 0u};
+        }
+    }
+  };
+
+  const float c2 = p.scale_log2;  // > 0, so the maximum commutes with the scaling
+  auto compute = [&](int pair) __attribute__((always_inline)) {
+    const int kbase = t0 + 32 * pair;
+    const bool full = kbase + 32 <= t1;
     // S^T for both pages
     f32x4_t sc[2];
 #pragma unroll
@@ -744,16 +779,18 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
         sc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], sc[pp], 0, 0, 0);
       }
     }
-    float mloc = kNegInf;
+    // raw scores (the scale goes into the exponent below); keys past t1
+    // only in the split's last pair
+    if (!full) {
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = kbase + 16 * pp + 4 * q4 + i < t1;
-        const float v = ok ? sc[pp][i] * p.scale_log2 : kNegInf;
-        sc[pp][i] = v;
-        mloc = fmaxf(mloc, v);
-      }
+        for (int i = 0; i < 4; ++i)
+          sc[pp][i] = kbase + 16 * pp + 4 * q4 + i < t1 ? sc[pp][i] : kNegInf;
+    }
+    float mloc = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mloc *= c2;
     if (__builtin_amdgcn_ballot_w64(mloc > m + C::kLazy) != 0) {
       float mm = fmaxf(mloc, xor_lane(mloc, 16));
       mm = fmaxf(mm, xor_lane(mm, 32));
@@ -764,15 +801,15 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
       for (int b = 0; b < DB; ++b) acc[b] *= alpha;
       m = mnew;
     }
-    const float mu = safe_max(m);
+    const float nmu = -safe_max(m);
     // The row sum adds the same bf16 weights the PV product uses, so the
     // normalised weights sum to one: a dominant weight's rounding cancels
     // instead of scaling the whole output.
     uint32_t pw[4];
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-      const float e0 = fast_exp2(sc[pp][0] - mu), e1 = fast_exp2(sc[pp][1] - mu);
-      const float e2 = fast_exp2(sc[pp][2] - mu), e3 = fast_exp2(sc[pp][3] - mu);
+      const float e0 = fast_exp2(fmaf(sc[pp][0], c2, nmu)), e1 = fast_exp2(fmaf(sc[pp][1], c2, nmu));
+      const float e2 = fast_exp2(fmaf(sc[pp][2], c2, nmu)), e3 = fast_exp2(fmaf(sc[pp][3], c2, nmu));
       pw[2 * pp] = pack_bf16(e0, e1);
       pw[2 * pp + 1] = pack_bf16(e2, e3);
       l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[2 * pp]), kOnes2, l, false);
@@ -796,22 +833,28 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
     }
   };
 
-  // Double-buffered software pipeline with a straight-line steady state, so
-  // the wait for one buffer's loads leaves the other buffer's loads in flight.
+  // Two register buffers, both always in flight: a pair's registers are
+  // reloaded with the pair after next as soon as they are staged in LDS,
+  // before the pair is used, so the wave keeps two pairs (32 keys x K and V
+  // each) of loads outstanding while it computes.  The scheduling barriers
+  // keep the compiler from sinking the loads below the computation.
+  // The loop runs an even number of pairs: a pair past the split's last has
+  // every key masked and adds exact zeros, and its loads touch no memory.
+  // With no branch inside, the loads of each buffer stay in issue order and
+  // the compiler waits for exactly the pair it stages.
   issue(kr[0], vr[0], 0);
-  int i = 0;
-  for (; i + 2 < npair; i += 2) {
-    issue(kr[1], vr[1], i + 1);
-    consume(kr[0], vr[0], i);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(kr[1], vr[1], 1);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < npair; i += 2) {
+    stage(kr[0], vr[0], i);
     issue(kr[0], vr[0], i + 2);
-    consume(kr[1], vr[1], i + 1);
-  }
-  if (i + 1 < npair) {
-    issue(kr[1], vr[1], i + 1);
-    consume(kr[0], vr[0], i);
-    consume(kr[1], vr[1], i + 1);
-  } else {
-    consume(kr[0], vr[0], i);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(i);
+    stage(kr[1], vr[1], i + 1);
+    issue(kr[1], vr[1], i + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(i + 1);
   }
 
   // l over the four key quads of each head column
@@ -881,8 +924,8 @@ DEV void decode_wave_mfma4(const PodParams& p, int wt, char* lds, int* wpids) {
   S = __builtin_amdgcn_readfirstlane(S);
   base = __builtin_amdgcn_readfirstlane(base);
   const int L = min(p.ctx[r], p.ctx_cap);
-  const int t0 = s * p.T;
-  const int t1 = min(t0 + p.T, L);
+  int t0, t1;
+  unit_range(L, p.T, p.T2, p.tail_k, s, t0, t1);
   const int npg = (t1 - t0 + kPageSize - 1) / kPageSize;
   const int kk = lane & 15, q4 = lane >> 4;       // MFMA roles: key / head column, quad
   const int lrow = lane / C::CHR, lchk = lane % C::CHR;  // load role: row in group, chunk

@@ -74,6 +74,7 @@ struct Limits {
   int policy = kPolicyCuBalanced;
   int slots_x256 = 0;  // prefill slots per CU for the CU-balanced policy; 0: from the batch
   int split_tokens = 0;  // decode tokens per wave task; 0: from the batch
+  int tail_split_tokens = 0;  // decode tail split length; 0: no tail splits
   bool persistent = false;  // fused launch as a resident grid looping over the queues
   bool record_roles = false;  // fused launches write one record per task (role trace)
   int num_cus = 0;
@@ -119,7 +120,8 @@ struct Plan {
   int d_max = 0;        // longest decode context
   int d_median = 0;     // median decode context
   int64_t d_total = 0;  // sum of decode contexts
-  int d_full = 0;       // decode units that are full T-token splits
+  int T2 = 0, tail_k = 0;  // short (tail) split length, long splits moved to the tail (pod_units.h)
+  int d_long = 0;       // decode units of the long phase (numbered first)
   // fused scheduling
   int share_num = 0, share_den = 1, cu_prefill_x256 = 0, policy = 0;
   bool persistent = false;  // the fused launch is a resident grid of workgroups

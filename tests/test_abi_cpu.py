@@ -96,6 +96,7 @@ def test_plan_invariants_on_configs(cid):
     # decode: every (request, kv head) split into ceil(L / T) one-wave units
     T = st["decode_split_tokens"]
     assert T % 16 == 0 and (256 if spec["dtype"] == "bf16" else 64) <= T <= 4096
+    assert st["decode_tail_split_tokens"] == 0  # no tail splits unless asked for
     assert st["decode_wave_tasks"] == hkv * sum(-(-int(L) // T) for L in lens)
     assert st["decode_wg_tasks"] == -(-st["decode_wave_tasks"] // 4)
     assert st["grid"] == st["prefill_tasks"] + st["decode_wg_tasks"]
@@ -123,11 +124,30 @@ def test_forced_decode_split_tokens():
     lens = [5000, 300, 16384]
     for T in (256, 1024, 4096):
         st = plan(_cfg(3, decode_split_tokens=T), pod.MODE_HYBRID, _prefill(512, 1024), _decode(lens))
-        assert st["decode_split_tokens"] == T
+        assert st["decode_split_tokens"] == T and st["decode_tail_split_tokens"] == 0
         assert st["decode_wave_tasks"] == 8 * sum(-(-L // T) for L in lens)
     for bad in (100, 255, 4112, 1000, -16):  # bf16: multiples of 16 in 256 .. 4096
         with pytest.raises(pod.PodAttnError) as e:
             plan(_cfg(3, decode_split_tokens=bad), pod.MODE_DECODE, None, _decode(lens))
+        assert e.value.status == pod.POD_ERR_INVALID_ARG
+
+
+def test_forced_tail_split_tokens():
+    # 5000 = one long split of 4096 is not kept (the last full split joins the
+    # tail): 5000 in 512-token pieces -> 10; 300 -> 1; 16384 = 3 long + 8
+    lens = [5000, 300, 16384]
+    st = plan(_cfg(3, decode_split_tokens=4096, decode_tail_split_tokens=512), pod.MODE_DECODE, None,
+              _decode(lens))
+    assert st["decode_tail_split_tokens"] == 512
+    assert st["decode_wave_tasks"] == 8 * (10 + 1 + 11)
+    # a tail split not below the split itself means no tail splits
+    st = plan(_cfg(3, decode_split_tokens=1024, decode_tail_split_tokens=1024), pod.MODE_DECODE, None,
+              _decode(lens))
+    assert st["decode_tail_split_tokens"] == 0
+    assert st["decode_wave_tasks"] == 8 * sum(-(-L // 1024) for L in lens)
+    for bad in (100, 255, 4112, 1000, -1):
+        with pytest.raises(pod.PodAttnError) as e:
+            plan(_cfg(3, decode_tail_split_tokens=bad), pod.MODE_DECODE, None, _decode(lens))
         assert e.value.status == pod.POD_ERR_INVALID_ARG
 
 
@@ -138,6 +158,7 @@ def test_decode_split_is_the_same_in_every_mode():
     a = plan(cfg, pod.MODE_HYBRID, _prefill(256, 2048), _decode(lens))
     b = plan(cfg, pod.MODE_DECODE, None, _decode(lens))
     assert a["decode_split_tokens"] == b["decode_split_tokens"]
+    assert a["decode_tail_split_tokens"] == b["decode_tail_split_tokens"]
     assert a["decode_wave_tasks"] == b["decode_wave_tasks"]
 
 
