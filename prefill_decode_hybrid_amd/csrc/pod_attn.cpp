@@ -215,7 +215,7 @@ void fill_params(const pod::Shape& s, float sm_scale, char* ws, const pod::Works
     p.tail_k = pl.tail_k;
     p.d_wave_tasks = pl.d_wave_tasks;
     p.d_units = pl.d_wave_tasks / s.hkv;
-    p.d_long = pl.d_long;
+    for (int ph = 0; ph <= pod::kUnitPhases; ++ph) p.phase_start[ph] = pl.phase_start[ph];
     p.ctx_cap = pl.d_max;
     p.d_wg_tasks = pl.d_wg_tasks;
   }

@@ -341,16 +341,17 @@ struct DecFrag {
 // more splits than the plan allowed for, and a unit whose records would
 // fall outside the plan's (possible only if the device lengths differ from
 // the host copy the launch was planned from) is dropped instead of written.
+template <int RB>
 DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S, int& base) {
   const int lane = lane_id();
-  const bool sp = unit >= p.d_long;
-  const uint32_t u = (uint32_t)(sp ? unit - p.d_long : unit);
+  const int ph = unit_phase_of(p.phase_start, unit_phases(p.tail_k, RB), unit);
+  const uint32_t u = (uint32_t)(unit - p.phase_start[ph]);
   uint32_t key_acc = 0, base_acc = 0;
   for (int c0 = 0; c0 < p.N; c0 += kUnitScanLanes) {
     const int idx = c0 + lane;
     int L = idx < p.N ? min(p.ctx[idx], p.ctx_cap) : 0;
     L = max(L, 0);
-    const uint32_t own = unit_pack(L, p.T, p.T2, p.tail_k, sp);
+    const uint32_t own = unit_pack(L, p.T, p.T2, p.tail_k, ph, RB);
     uint32_t incl = own;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -362,7 +363,7 @@ DEV bool locate_unit(const PodParams& p, int unit, int& r, int& s, int& S, int& 
       const uint64_t hit = __ballot(key_acc + unit_phase(incl) > u);
       const int first = __builtin_ctzll(hit);
       r = c0 + first;
-      unit_select(u, sp, key_acc, base_acc, __shfl(own, first, 64), __shfl(incl, first, 64), s, S, base);
+      unit_select(u, ph, key_acc, base_acc, __shfl(own, first, 64), __shfl(incl, first, 64), s, S, base);
       return base >= 0 && base + S <= p.d_units;
     }
     key_acc += unit_phase(total);
@@ -403,7 +404,7 @@ DEV void decode_finish(const PodParams& p, int r, int S, int base, int g, float*
   if (lane_id() == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class E, int D, int G, int PF>
+template <class E, int D, int G, int PF, int RB>
 DEV void decode_wave(const PodParams& p, int wt, float* wl) {
   using Fr = DecFrag<E, D>;
   constexpr int EPL = Fr::EPL, DW = Fr::DW;
@@ -412,7 +413,7 @@ DEV void decode_wave(const PodParams& p, int wt, float* wl) {
   const int g = wt % hkv;
   const int unit = wt / hkv;
   int r, s, S, base;
-  if (!locate_unit(p, unit, r, s, S, base)) return;
+  if (!locate_unit<RB>(p, unit, r, s, S, base)) return;
   r = __builtin_amdgcn_readfirstlane(r);
   s = __builtin_amdgcn_readfirstlane(s);
   S = __builtin_amdgcn_readfirstlane(S);
@@ -636,7 +637,7 @@ DEV int vsw_prefill(int row) { return 4 * ((row / (16 / CH)) & (CH / 4 - 1)); }
 template <int CH>
 DEV int vsw_decode(int row) { return 2 * ((row / (16 / CH)) & (CH / 2 - 1)); }
 
-template <int D, int G>
+template <int D, int G, int RB>
 DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   using C = DecMfma<D>;
   constexpr int KC = C::KC, DB = C::DB, NI = C::NI;
@@ -645,7 +646,7 @@ DEV void decode_wave_mfma(const PodParams& p, int wt, char* lds) {
   const int g = wt % hkv;
   const int unit = wt / hkv;
   int r, s, S, base;
-  if (!locate_unit(p, unit, r, s, S, base)) return;
+  if (!locate_unit<RB>(p, unit, r, s, S, base)) return;
   r = __builtin_amdgcn_readfirstlane(r);
   s = __builtin_amdgcn_readfirstlane(s);
   S = __builtin_amdgcn_readfirstlane(S);
@@ -909,7 +910,7 @@ struct DecMfma4 {
   static constexpr float kLazy = 8.0f;
 };
 
-template <int D, int G>
+template <int D, int G, int RB>
 DEV void decode_wave_mfma4(const PodParams& p, int wt, char* lds, int* wpids) {
   using C = DecMfma4<D>;
   constexpr int KC = C::KC, DB = C::DB, NI = C::NI;
@@ -918,7 +919,7 @@ DEV void decode_wave_mfma4(const PodParams& p, int wt, char* lds, int* wpids) {
   const int g = wt % hkv;
   const int unit = wt / hkv;
   int r, s, S, base;
-  if (!locate_unit(p, unit, r, s, S, base)) return;
+  if (!locate_unit<RB>(p, unit, r, s, S, base)) return;
   r = __builtin_amdgcn_readfirstlane(r);
   s = __builtin_amdgcn_readfirstlane(s);
   S = __builtin_amdgcn_readfirstlane(S);
@@ -1087,25 +1088,27 @@ DEV void decode_wave_mfma4(const PodParams& p, int wt, char* lds, int* wpids) {
   decode_finish<Bf16, D, G, 4>(p, r, S, base, g, reinterpret_cast<float*>(lds));
 }
 
-template <int D, int G>
+// RB: remainder phases of the unit numbering (1 in fused launches,
+// kRemBuckets in decode-only launches; the plan numbers the units alike)
+template <int D, int G, int RB = 1>
 DEV void decode_wg4(const PodParams& p, int wg_task, const LdsBufs& lb) {
   const int wt = wg_task * kWavesPerWG + wave_id();
   if (wt >= p.d_wave_tasks) return;
   const int w = wave_id();
   char* buf = w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3];
-  decode_wave_mfma4<D, G>(p, wt, buf, lb.pids + w * (kSplitIdRegs * 64));
+  decode_wave_mfma4<D, G, RB>(p, wt, buf, lb.pids + w * (kSplitIdRegs * 64));
 }
 
-template <class E, int D, int G, int PF>
+template <class E, int D, int G, int PF, int RB = 1>
 DEV void decode_wg(const PodParams& p, int wg_task, const LdsBufs& lb) {
   const int wt = wg_task * kWavesPerWG + wave_id();
   if (wt >= p.d_wave_tasks) return;
   const int w = wave_id();
   char* buf = w == 0 ? lb.st[0] : w == 1 ? lb.st[1] : w == 2 ? lb.st[2] : lb.st[3];
   if constexpr (E::bytes == 2)
-    decode_wave_mfma<D, G>(p, wt, buf);
+    decode_wave_mfma<D, G, RB>(p, wt, buf);
   else
-    decode_wave<E, D, G, PF>(p, wt, reinterpret_cast<float*>(buf));
+    decode_wave<E, D, G, PF, RB>(p, wt, reinterpret_cast<float*>(buf));
 }
 
 // ---------------------------------------------------------- prefill (a2, a4)
@@ -1948,7 +1951,7 @@ __global__ __launch_bounds__(256, (decode_min_blocks<E, G>())) void pod_decode_k
   __shared__ __attribute__((aligned(16))) char dbuf2[W];
   __shared__ __attribute__((aligned(16))) char dbuf3[W];
   const LdsBufs lb{{dbuf0, dbuf1, dbuf2, dbuf3}, nullptr, nullptr};
-  decode_wg<E, D, G, decode_pf<E>()>(p, blockIdx.x, lb);
+  decode_wg<E, D, G, decode_pf<E>(), kRemBuckets>(p, blockIdx.x, lb);
 }
 
 // Per-XCD task queues: queue x of `heads` holds tasks x, x+8, x+16, ... of
@@ -2188,7 +2191,7 @@ __global__ __launch_bounds__(256, 4) void pod_decode4_kernel(PodParams p) {
   __shared__ __attribute__((aligned(16))) char dbuf3[W];
   __shared__ int dpids[kWavesPerWG * kSplitIdRegs * 64];
   const LdsBufs lb{{dbuf0, dbuf1, dbuf2, dbuf3}, dpids, nullptr};
-  decode_wg4<D, G>(p, blockIdx.x, lb);
+  decode_wg4<D, G, kRemBuckets>(p, blockIdx.x, lb);
 }
 
 // Persistent variant of the fused kernel: a grid of (CUs x resident

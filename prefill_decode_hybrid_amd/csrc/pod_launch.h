@@ -45,7 +45,7 @@ struct PodParams {
   int stride, N, d_units, d_wave_tasks, d_wg_tasks;
   int T, T2, tail_k; // long and short split lengths, long splits moved to the short phase (pod_units.h)
   int ctx_cap;       // device context lengths are clamped to this (the batch's largest host length)
-  int d_long;        // units of the long phase (numbered before the short ones)
+  int phase_start[kUnitPhases + 1];  // first decode unit of every phase (pod_units.h)
   float* d_part;     // records [kv head][unit]: [G][d] acc, [G] m, [G] l, 16-byte padded
   uint32_t* d_cnt;   // [request][kv head] arrival counters, 0 between calls
 

@@ -327,13 +327,29 @@ static int plan_wg(const Shape& s, const Limits& lim, int wg, int mode, const Pr
     // the kernels' unit scan holds at most kMaxSplitsPerRequest splits per
     // request; a request has at most ceil(L / T2) of them
     if (ceil_div(pl.d_max, pl.T2) > kMaxSplitsPerRequest) return POD_ERR_UNSUPPORTED;
-    int64_t units = 0, n_long = 0;
-    for (int r = 0; r < d.N; ++r) {
-      const int a = unit_long(d.ctx_host[r], pl.T, pl.tail_k);
-      n_long += a;
-      units += a + unit_short(d.ctx_host[r], pl.T, pl.T2, pl.tail_k);
+    // Units are numbered phase by phase: the long splits, then the tail
+    // splits (k = 1) or the remainders.  A decode-only launch takes the
+    // remainders longest first in eight length classes, which shortened its
+    // end on 256 log-uniform contexts (decode alone 1088-1094 -> 1050-1059
+    // us); a fused launch keeps request order, where the prefill fills the
+    // decode's end and the length classes cost 1-3% in the lookup.  The
+    // order never changes a result: a split's record index does not depend
+    // on it.
+    pl.rem_buckets = (pl.has_d && !pl.has_p) ? kRemBuckets : 1;
+    const int np = unit_phases(pl.tail_k, pl.rem_buckets);
+    int64_t per_phase[kUnitPhases] = {};
+    for (int r = 0; r < d.N; ++r)
+      for (int ph = 0; ph < np; ++ph)
+        per_phase[ph] += unit_count(d.ctx_host[r], pl.T, pl.T2, pl.tail_k, ph, pl.rem_buckets);
+    int64_t units = 0;
+    for (int ph = 0; ph < np; ++ph) units += per_phase[ph];
+    if (units > (1LL << 30)) return POD_ERR_WORKSPACE;
+    int64_t acc = 0;
+    for (int ph = 0; ph < np; ++ph) {
+      pl.phase_start[ph] = (int)acc;
+      acc += per_phase[ph];
     }
-    pl.d_long = (int)n_long;
+    for (int ph = np; ph <= kUnitPhases; ++ph) pl.phase_start[ph] = (int)acc;
     int64_t wt = units * s.hkv;
     if (wt > lim.cap_wave_tasks || wt > (1LL << 30)) return POD_ERR_WORKSPACE;
     pl.d_wave_tasks = (int)wt;

@@ -5,8 +5,11 @@ with a plain enumeration of the units for every batch the planner accepts.
 A request of L keys is cut into long splits of T keys from its start and a
 tail cut into short splits of T2 keys: with k = 0 the tail is the remainder
 L mod T (one split); with k = 1 it also takes the last full long split.
-Units are numbered long phase first (every request's long splits, request
-by request, then every request's short splits); the record of (r, s) is
+Units are numbered long splits first (every request's, request by request);
+then, with k = 0, the remainders in request order (fused launches) or
+longest first in eight length classes ([7T/8, T) first, [0, T/8) last;
+request by request within a class; decode-only launches), or, with k = 1,
+every request's short splits.  The record of (r, s) is
 base(r) + s with base(r) = the splits of the requests before r.  The lookup
 scans packed per-request counts 64 requests at a time
 (prefill_decode_hybrid_amd/csrc/pod_units.h); the cases here include the
@@ -33,8 +36,8 @@ def mirror(tmp_path_factory):
     exe = str(tmp_path_factory.mktemp("scan") / "unit_scan_mirror")
     subprocess.run([gxx, "-O2", "-std=c++17", "-Wall", "-Werror", SRC, "-o", exe], check=True)
 
-    def run(lens, T, T2=None, k=0):
-        inp = f"{len(lens)} {T} {T2 or T} {k}\n" + " ".join(str(int(x)) for x in lens) + "\n"
+    def run(lens, T, T2=None, k=0, nb=1):
+        inp = f"{len(lens)} {T} {T2 or T} {k} {nb}\n" + " ".join(str(int(x)) for x in lens) + "\n"
         out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout.split("\n")
         return [ln for ln in out if ln]
     return run
@@ -52,8 +55,10 @@ def split_ranges(L, T, T2, k):
     return out, a
 
 
-def enumerate_units(lens, T, T2=None, k=0):
-    """The numbering written out: long splits request by request, then short ones."""
+def enumerate_units(lens, T, T2=None, k=0, nb=1):
+    """The numbering written out: long splits request by request, then the
+    remainders (k = 0: in request order for nb = 1, by length class for
+    nb = 8) or every request's short splits (k = 1)."""
     T2 = T2 or T
     lens = [int(x) for x in lens]
     per = [split_ranges(L, T, T2, k) for L in lens]
@@ -63,15 +68,28 @@ def enumerate_units(lens, T, T2=None, k=0):
     for r, (rng, a) in enumerate(per):
         for s in range(a):
             units.append((r, s, S[r], base[r]) + rng[s])
-    for r, (rng, a) in enumerate(per):
-        for s in range(a, S[r]):
-            units.append((r, s, S[r], base[r]) + rng[s])
+    if k == 0:
+        classes = range(7, -1, -1) if nb == 8 else [None]
+        for cls in classes:  # remainder length class floor(8 rem / T), longest first
+            for r, (rng, a) in enumerate(per):
+                if S[r] > a:
+                    rem = rng[a][1] - rng[a][0]
+                    if cls is None or (8 * rem) // T == cls:
+                        units.append((r, a, S[r], base[r]) + rng[a])
+    else:
+        for r, (rng, a) in enumerate(per):
+            for s in range(a, S[r]):
+                units.append((r, s, S[r], base[r]) + rng[s])
     return units
 
 
-def check(mirror, lens, T, T2=None, k=0):
-    got = mirror(lens, T, T2, k)
-    want = enumerate_units(lens, T, T2, k)
+def check(mirror, lens, T, T2=None, k=0, nb=None):
+    if nb is None:  # both numberings of the remainders
+        for b in (1, 8):
+            check(mirror, lens, T, T2, k, b)
+        return
+    got = mirror(lens, T, T2, k, nb)
+    want = enumerate_units(lens, T, T2, k, nb)
     assert got[-1] == "miss", "a unit past the last must not be found"
     got = [tuple(int(x) for x in ln.split()) for ln in got[:-1]]
     assert len(got) == len(want)

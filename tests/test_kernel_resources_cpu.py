@@ -62,9 +62,10 @@ def test_launched_kernels_use_no_scratch(res):
         if short is None and short4 is None:  # the fill kernel of the allocation-free entry point
             assert "pod_zero_kernel" in name, name
         if short4 is not None and short4[0] == "pod_hybrid4_kernel" and short4[1] == "128":
-            # one 8-byte value is kept in scratch across the decode loop and
-            # reloaded once after it (the fused 128-register kernel holds both roles)
-            assert r["scratch"] <= 16, (name, r)
+            # a few values are kept in scratch across the decode loop (stored
+            # once before it, reloaded once after it; the fused 128-register
+            # kernel holds both roles)
+            assert r["scratch"] <= 32, (name, r)
         elif short is None or short[0] != "pod_persistent_kernel":
             assert r["scratch"] == 0, (name, r)
 
