@@ -31,14 +31,14 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", range(len(CASES)))
-def test_tail_splits_match_the_oracle(case):
+@pytest.mark.parametrize("case,wg", [(c, 2) for c in range(len(CASES))] + [(0, 4), (2, 4)])
+def test_tail_splits_match_the_oracle(case, wg):
     sp, T, T2 = CASES[case]
-    run = Run(inputs.make_batch(sp, seed=21), decode_split_tokens=T, decode_tail_split_tokens=T2)
+    run = Run(inputs.make_batch(sp, seed=21), decode_split_tokens=T, decode_tail_split_tokens=T2, wg_per_cu=wg)
     try:
         op, od = run.hybrid()
         st = run.att.stats()
-        say(f"{sp['name']} T {T} T2 {T2}: plan {st}")
+        say(f"{sp['name']} T {T} T2 {T2} wg {wg}: plan {st}")
         assert st["decode_split_tokens"] == T and st["decode_tail_split_tokens"] == T2
         check_against_oracle(run, op, od, label=f"{sp['name']} tail splits")
         sp_, sd_ = run.separate()
