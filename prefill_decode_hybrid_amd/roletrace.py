@@ -8,10 +8,12 @@ the Silicon & Systems digest asks the runtime to report the virtual-CTA mix
 it achieved).  From the records this module reports, per role, the tasks and
 the CUs they ran on, per XCD the task counts, the mean number of prefill and
 decode workgroups resident per CU over the launch (to set beside the plan's
-prefill slots per CU), and the share of CU-busy time during which a CU ran
-both roles at once.
+prefill slots per CU), the share of CU-busy time during which a CU ran
+both roles at once, and a timeline of running workgroups with the decode's
+approximate stream rate (each decode task's K/V bytes spread evenly over
+its own start-to-end time).
 
-    python -m prefill_decode_hybrid_amd.roletrace --config 3 [--wg-per-cu 2] [--out profiles]
+    python -m prefill_decode_hybrid_amd.roletrace --config 3 [--wg-per-cu 2] [--buckets 20] [--out profiles]
 """
 from __future__ import annotations
 
@@ -28,8 +30,44 @@ def xcd_of(key: int) -> int:
     return (key >> 8) & 7
 
 
-def summarize(records, num_cus: int = 256) -> dict:
-    """records: iterable of (cu_key, role, task, start, end)."""
+def unit_tokens(lens, T: int, T2: int = 0, k: int = 0) -> list:
+    """Keys of every decode unit in the order a fused launch numbers them:
+    each request's long splits of T keys (request by request), then its
+    tail: with k = 0 the remainder as one unit, with k = 1 the last full
+    split and the remainder in units of T2 keys (request by request)."""
+    longs, tails = [], []
+    for L in (int(x) for x in lens):
+        F = L // T
+        a = F - k if F > k else 0
+        longs += [T] * a
+        tail = L - a * T
+        if k == 0:
+            if tail > 0:
+                tails.append(tail)
+        else:
+            while tail > 0:
+                tails.append(min(T2, tail))
+                tail -= T2
+    return longs + tails
+
+
+def decode_task_bytes(lens, T: int, T2: int, hkv: int, head_dim: int, elem_bytes: int,
+                      waves_per_wg: int = 4) -> list:
+    """K and V bytes each decode workgroup task of a fused launch streams:
+    wave task w is (unit w // hkv, kv head w % hkv), a workgroup task runs
+    waves_per_wg consecutive wave tasks."""
+    units = unit_tokens(lens, T, T2, 1 if T2 else 0)
+    row = 2 * head_dim * elem_bytes  # one key's K and V row of one kv head
+    n_wave = len(units) * hkv
+    out = []
+    for t in range((n_wave + waves_per_wg - 1) // waves_per_wg):
+        out.append(sum(units[w // hkv] * row for w in range(t * waves_per_wg, min(n_wave, (t + 1) * waves_per_wg))))
+    return out
+
+
+def summarize(records, num_cus: int = 256, buckets: int = 10, decode_bytes=None) -> dict:
+    """records: iterable of (cu_key, role, task, start, end); decode_bytes:
+    K/V bytes of each decode workgroup task, for the timeline's stream rate."""
     recs = [tuple(int(x) for x in r) for r in records]
     if not recs:
         return {"tasks": 0}
@@ -64,9 +102,11 @@ def summarize(records, num_cus: int = 256) -> dict:
                     any_time += t - last
                 last = t
             n[role] += d
-    # mean running workgroups per CU of each role in ten equal time buckets
-    nb = 10
+    # mean running workgroups per CU of each role in equal time buckets, and
+    # the decode's bytes per bucket (each task's spread over its own time)
+    nb = max(1, int(buckets))
     tl = [[0, 0] for _ in range(nb)]
+    db = [0.0] * nb
     width = span / nb
     for key, role, task, t0, t1 in recs:
         for k in range(nb):
@@ -74,8 +114,14 @@ def summarize(records, num_cus: int = 256) -> dict:
             ov = min(t1, hi) - max(t0, lo)
             if ov > 0:
                 tl[k][role] += ov
-    timeline = [{"prefill": round(a / (num_cus * width), 3), "decode": round(b / (num_cus * width), 3)}
-                for a, b in tl]
+                if role == 1 and decode_bytes is not None and t1 > t0:
+                    db[k] += decode_bytes[task] * ov / (t1 - t0)
+    timeline = []
+    for k, (a, b) in enumerate(tl):
+        e = {"prefill": round(a / (num_cus * width), 3), "decode": round(b / (num_cus * width), 3)}
+        if decode_bytes is not None:
+            e["decode_tb_s"] = round(db[k] / (width * TICK_US * 1e-6) / 1e12, 2)
+        timeline.append(e)
     return {
         "tasks": len(recs),
         "span_us": round(span * TICK_US, 1),
@@ -99,7 +145,10 @@ def main(argv=None):
     ap.add_argument("--slots-x256", type=int, default=0)
     ap.add_argument("--decode-split-tokens", type=int, default=0)
     ap.add_argument("--prefill-splits", type=int, default=0)
-    ap.add_argument("--out", default="", help="write role_mix_<workload>.md and .json here")
+    ap.add_argument("--decode-tail-split-tokens", type=int, default=0)
+    ap.add_argument("--buckets", type=int, default=10, help="time buckets of the timeline")
+    ap.add_argument("--tag", default="", help="suffix of the output file name")
+    ap.add_argument("--out", default="", help="write role_mix_<workload>[_<tag>].md here")
     a = ap.parse_args(argv)
 
     import torch
@@ -115,6 +164,7 @@ def main(argv=None):
     att = pod.PodAttention(pod.config_for_batch(b, wg_per_cu=a.wg_per_cu, policy=a.policy,
                                                 prefill_slots_x256=a.slots_x256, record_roles=1,
                                                 decode_split_tokens=a.decode_split_tokens,
+                                                decode_tail_split_tokens=a.decode_tail_split_tokens,
                                                 prefill_splits=a.prefill_splits))
     op, od = torch.empty_like(dev.q_prefill), torch.empty_like(dev.q_decode)
     # as in the benchmark: the L2s and the Infinity Cache are flushed (1 GiB
@@ -125,7 +175,11 @@ def main(argv=None):
         att.hybrid(dev, op, od, ctx)
     torch.cuda.synchronize()
     plan = att.stats()
-    s = summarize(att.role_trace(), plan["num_cus"])
+    dbytes = decode_task_bytes(b.context_lens.tolist(), plan["decode_split_tokens"],
+                               plan["decode_tail_split_tokens"], b.num_kv_heads, b.head_dim,
+                               2 if b.spec["dtype"] == "bf16" else 4)
+    assert len(dbytes) == plan["decode_wg_tasks"], "decode task numbering differs from the plan"
+    s = summarize(att.role_trace(), plan["num_cus"], a.buckets, dbytes)
     att.close()
     workload = f"config{a.config}_{b.spec['name']}"
     out = {"workload": workload, "wg_per_cu": plan["wg_per_cu"], "policy": a.policy,
@@ -147,12 +201,16 @@ def main(argv=None):
         lines += ["", "| XCD | prefill tasks | decode tasks |", "|---|---|---|"]
         for x, v in s["tasks_per_xcd"].items():
             lines.append(f"| {x} | {v['prefill']} | {v['decode']} |")
-        lines += ["", "Running workgroups per CU over the launch, in tenths of its span:", "",
-                  "| tenth | prefill | decode | idle slots |", "|---|---|---|---|"]
+        width = s["span_us"] / a.buckets
+        lines += ["", f"Running workgroups per CU over the launch in {a.buckets} equal parts of its span "
+                  f"({width:.1f} us each), and the decode's stream rate (each decode task's K/V bytes "
+                  "spread evenly over its own start-to-end time, so an approximation):", "",
+                  "| part | from us | prefill | decode | idle slots | decode TB/s |", "|---|---|---|---|---|---|"]
         for k, v in enumerate(s["timeline_wgs_per_cu"]):
-            lines.append(f"| {k + 1} | {v['prefill']} | {v['decode']} | "
-                         f"{round(plan['wg_per_cu'] - v['prefill'] - v['decode'], 3)} |")
-        open(os.path.join(a.out, f"role_mix_{workload}.md"), "w").write("\n".join(lines) + "\n")
+            lines.append(f"| {k + 1} | {k * width:.0f} | {v['prefill']} | {v['decode']} | "
+                         f"{round(plan['wg_per_cu'] - v['prefill'] - v['decode'], 3)} | {v.get('decode_tb_s', '')} |")
+        name = f"role_mix_{workload}" + (f"_{a.tag}" if a.tag else "")
+        open(os.path.join(a.out, name + ".md"), "w").write("\n".join(lines) + "\n")
 
 
 if __name__ == "__main__":
