@@ -2237,6 +2237,10 @@ __global__ __launch_bounds__(256, 2) void pod_persistent_kernel(PodParams p) {
 template <class E, int D, int G>
 static int launch_t(int which, const PodParams& p, const Plan& pl, hipStream_t s) {
   const dim3 block(256);
+  // the decode units were numbered for the kernel family that runs them:
+  // request-order remainders in fused launches, length classes in
+  // decode-only ones (the kernels fix the class count at compile time)
+  if (pl.has_d && pl.rem_buckets != (which == kKernelDecode ? kRemBuckets : 1)) return (int)hipErrorInvalidValue;
   if (pl.wg_per_cu == 4) {
     if constexpr (E::bytes == 2) {
       switch (which) {
