@@ -53,6 +53,37 @@ def work_counts(b):
                 bytes_total=bytes_kv + bytes_qo)
 
 
+def measured_peaks(torch, pod, num_cus, steps=5):
+    """What the chip sustains: a plain HBM read of 4 GiB (well above the
+    256 MB Infinity Cache, so every byte comes from HBM) and an MFMA loop
+    of ~2 ms, both with two workgroups per CU, timed with HIP events on the
+    launch stream; medians of `steps` calls after one warm-up each."""
+    wgs = 2 * num_cus
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    iters = 4096
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ts) * 1e-3
+
+    t_read = timed(lambda: pod.pod_attn_peak_read(buf, nbytes, wgs, sink))
+    t_mfma = timed(lambda: pod.pod_attn_peak_mfma(wgs, iters, sink))
+    flops = wgs * 4 * iters * pod.PEAK_MFMA_FLOPS_PER_ITER_WAVE
+    del buf
+    return {"hbm_read_GBps": round(nbytes / t_read / 1e9, 1), "mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "read_bytes": nbytes, "mfma_flops": flops, "workgroups": wgs}
+
+
 def load_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None if
     they are missing or were taken on different kernel machine code."""
@@ -356,6 +387,9 @@ def main():
         host_us.append((time.perf_counter() - a) * 1e6)
     torch.cuda.synchronize()
 
+    peaks = measured_peaks(torch, pod, plan["num_cus"])
+    log(f"[bench] measured peaks {peaks}")
+
     w = work_counts(batch)
     med = statistics.median(t_fused) * 1e-3  # seconds
     bf16 = batch.spec["dtype"] == "bf16"
@@ -400,6 +434,13 @@ def main():
                              "t_hbm_us": round(t_hbm * 1e6, 2), "frac": round(max(t_mfma, t_hbm) / med, 4),
                              "algorithmic_bytes": w["bytes_total"], "prefill_flops": w["f_prefill"],
                              "decode_flops": w["f_decode"]},
+        # the same roofline against what a plain HBM read and an MFMA loop sustain on this GPU
+        # (bf16 batches; the fp32 path has no MFMA loop here)
+        "measured_roofline": dict(peaks, **({
+            "t_roof_us": round(max(w["f_prefill"] / (peaks["mfma_bf16_TFLOPs"] * 1e12),
+                                   w["bytes_total"] / (peaks["hbm_read_GBps"] * 1e9)) * 1e6, 2),
+            "frac": round(max(w["f_prefill"] / (peaks["mfma_bf16_TFLOPs"] * 1e12),
+                              w["bytes_total"] / (peaks["hbm_read_GBps"] * 1e9)) / med, 4)} if bf16 else {})),
         "tflops": round((w["f_prefill"] + w["f_decode"]) / med / 1e12, 2),
         "fused": q(t_fused),
         # the speedups compare medians from one interleaved loop over the three modes

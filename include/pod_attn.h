@@ -306,6 +306,26 @@ int pod_attn_plan_varlen(const pod_attn_config *cfg, int32_t num_cus, int32_t mo
  * not record roles.  A diagnostic call: it synchronises the device. */
 int pod_attn_role_trace(pod_attn_handle *h, pod_attn_task_record *out, int32_t capacity, int32_t *count);
 
+/* Measured peaks, for a roofline fraction against what the chip sustains
+ * next to the published peaks (the reproduction test of the Silicon &
+ * Systems digest, "A reproduction and procurement test", asks for achieved
+ * memory bandwidth and tensor-core activity).  Both enqueue one kernel on
+ * `stream` and return at once; the caller times them with events.
+ *
+ * pod_attn_peak_read: `workgroups` workgroups of four waves read all `bytes`
+ * of device buffer `buf` once, each wave a contiguous slice of
+ * bytes / (4 workgroups) with nontemporal 16-byte loads.  The slice must be
+ * a multiple of 16384 bytes and at most 1 GiB (POD_ERR_INVALID_ARG
+ * otherwise).  `sink` is a device word written only if the XOR of the data
+ * equals 0x9e3779b9 (it keeps the loads; a zero-filled buffer never writes).
+ *
+ * pod_attn_peak_mfma: `workgroups` x 4 waves x `iters` x 16
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) in four independent chains per
+ * wave on register operands; `sink` as above. */
+int pod_attn_peak_read(const void *buf, int64_t bytes, int32_t workgroups, uint32_t *sink,
+                       pod_stream_t stream);
+int pod_attn_peak_mfma(int32_t workgroups, int32_t iters, uint32_t *sink, pod_stream_t stream);
+
 /* Copy the plan of the last successful compute call into *out. */
 int pod_attn_get_stats(const pod_attn_handle *h, pod_attn_stats *out);
 

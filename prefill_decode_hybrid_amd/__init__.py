@@ -28,7 +28,7 @@ POD_MAX_CHUNKS = 64
 EXPORTED = ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_prefill_only",
             "pod_attn_decode_only", "pod_attn_hybrid_noalloc", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
             "pod_attn_get_stats", "pod_attn_role_trace", "pod_attn_plan", "pod_attn_plan_varlen",
-            "pod_attn_status_string", "pod_attn_last_error")
+            "pod_attn_status_string", "pod_attn_last_error", "pod_attn_peak_read", "pod_attn_peak_mfma")
 
 
 class PodAttnConfig(ctypes.Structure):
@@ -117,10 +117,12 @@ def load(path: str = LIB_PATH):
     lib.pod_attn_status_string.restype = ctypes.c_char_p
     lib.pod_attn_last_error.argtypes = [P]
     lib.pod_attn_last_error.restype = ctypes.c_char_p
+    lib.pod_attn_peak_read.argtypes = [P, i64, i32, P, P]
+    lib.pod_attn_peak_mfma.argtypes = [i32, i32, P, P]
     for name in ("pod_attn_create", "pod_attn_destroy", "pod_attn_hybrid", "pod_attn_hybrid_noalloc",
-                 "pod_attn_prefill_only",
-                 "pod_attn_decode_only", "pod_attn_hybrid_noalloc", "pod_attn_hybrid_varlen", "pod_attn_prefill_only_varlen",
-                 "pod_attn_get_stats", "pod_attn_role_trace", "pod_attn_plan", "pod_attn_plan_varlen"):
+                 "pod_attn_prefill_only", "pod_attn_decode_only", "pod_attn_hybrid_varlen",
+                 "pod_attn_prefill_only_varlen", "pod_attn_get_stats", "pod_attn_role_trace", "pod_attn_plan",
+                 "pod_attn_plan_varlen", "pod_attn_peak_read", "pod_attn_peak_mfma"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -283,6 +285,26 @@ def pod_attn_plan_varlen(cfg: PodAttnConfig, num_cus: int, mode: int, prefill=No
     if rc != POD_OK:
         raise PodAttnError(rc, "pod_attn_plan_varlen")
     return st.as_dict()
+
+
+def pod_attn_peak_read(buf, nbytes: int, workgroups: int, sink, stream=None) -> None:
+    """Enqueue the HBM-read kernel over `nbytes` of device buffer `buf` (a
+    tensor or pointer); `sink` is a device uint32 word (tensor or pointer)."""
+    rc = load().pod_attn_peak_read(_ptr(buf) if hasattr(buf, "data_ptr") else buf, int(nbytes), int(workgroups),
+                                   _ptr(sink) if hasattr(sink, "data_ptr") else sink, _stream_ptr(stream))
+    if rc != POD_OK:
+        raise PodAttnError(rc, "pod_attn_peak_read")
+
+
+def pod_attn_peak_mfma(workgroups: int, iters: int, sink, stream=None) -> None:
+    """Enqueue the MFMA loop: workgroups x 4 waves x iters x 16 bf16 32x32x16 MFMAs."""
+    rc = load().pod_attn_peak_mfma(int(workgroups), int(iters), _ptr(sink) if hasattr(sink, "data_ptr") else sink,
+                                   _stream_ptr(stream))
+    if rc != POD_OK:
+        raise PodAttnError(rc, "pod_attn_peak_mfma")
+
+
+PEAK_MFMA_FLOPS_PER_ITER_WAVE = 16 * 2 * 32 * 32 * 16  # 16 MFMAs of 32x32x16 per loop iteration
 
 
 class PodAttention:

@@ -416,6 +416,21 @@ int pod_attn_prefill_only_varlen(pod_attn_handle* h, const void* k_pool, const v
   return rc ? rc : run(h, pod::kModePrefill, k_pool, v_pool, num_pages, pv, nullptr, stream);
 }
 
+int pod_attn_peak_read(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* sink, pod_stream_t stream) {
+  if (!buf || !sink || workgroups < 1 || bytes < 1) return POD_ERR_INVALID_ARG;
+  const int64_t waves = (int64_t)workgroups * pod::kWavesPerWG;
+  // each wave's slice: a whole number of 16 KB register buffers, at most 1 GiB
+  if (bytes % (waves * 16384) != 0 || bytes / waves > (int64_t(1) << 30)) return POD_ERR_INVALID_ARG;
+  const int e = pod::launch_peak_read(buf, (size_t)bytes, workgroups, sink, reinterpret_cast<hipStream_t>(stream));
+  return e == 0 ? POD_OK : POD_ERR_HIP;
+}
+
+int pod_attn_peak_mfma(int32_t workgroups, int32_t iters, uint32_t* sink, pod_stream_t stream) {
+  if (!sink || workgroups < 1 || iters < 1) return POD_ERR_INVALID_ARG;
+  const int e = pod::launch_peak_mfma(workgroups, iters, sink, reinterpret_cast<hipStream_t>(stream));
+  return e == 0 ? POD_OK : POD_ERR_HIP;
+}
+
 int pod_attn_role_trace(pod_attn_handle* h, pod_attn_task_record* out, int32_t capacity, int32_t* count) {
   if (!h || !count || capacity < 0 || (capacity > 0 && !out)) return POD_ERR_INVALID_ARG;
   if (!h->lay.trace_bytes) return POD_ERR_INVALID_ARG;  // the handle does not record roles

@@ -80,5 +80,10 @@ int scratch_address(int device, void** out);
 // Zero `bytes` (a multiple of 4) at `p` with a fill kernel (no memset node
 // in a captured graph).  Returns a hipError_t.
 int launch_zero(void* p, size_t bytes, hipStream_t s);
+// Measured-peak kernels: `bytes` of `buf` read by `workgroups` workgroups
+// (each wave a contiguous bytes / (4 workgroups) slice, a multiple of 16
+// KB), and `workgroups` x 4 waves x `iters` x 16 MFMAs of 32x32x16 bf16.
+int launch_peak_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, hipStream_t s);
+int launch_peak_mfma(int workgroups, int iters, uint32_t* sink, hipStream_t s);
 
 }  // namespace pod

@@ -457,3 +457,19 @@ def test_prefill_split_knobs():
         with pytest.raises(pod.PodAttnError) as e:
             plan(_cfg(3, **bad), pod.MODE_HYBRID, pa, da)
         assert e.value.status == pod.POD_ERR_INVALID_ARG
+
+
+def test_peak_kernels_validate_before_launch(lib):
+    # measured-peak entry points reject bad arguments without touching a device
+    inv = pod.POD_ERR_INVALID_ARG
+    assert lib.pod_attn_peak_read(None, 1 << 20, 4, FAKE, None) == inv
+    assert lib.pod_attn_peak_read(FAKE, 1 << 20, 4, None, None) == inv
+    assert lib.pod_attn_peak_read(FAKE, 0, 4, FAKE, None) == inv
+    assert lib.pod_attn_peak_read(FAKE, 1 << 20, 0, FAKE, None) == inv
+    # each wave's slice must be whole 16 KB buffers ...
+    assert lib.pod_attn_peak_read(FAKE, 4 * 16384 + 4096, 1, FAKE, None) == inv
+    # ... and at most 1 GiB
+    assert lib.pod_attn_peak_read(FAKE, 4 * ((1 << 30) + 16384), 1, FAKE, None) == inv
+    assert lib.pod_attn_peak_mfma(0, 8, FAKE, None) == inv
+    assert lib.pod_attn_peak_mfma(4, 0, FAKE, None) == inv
+    assert lib.pod_attn_peak_mfma(4, 8, None, None) == inv
