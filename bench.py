@@ -14,6 +14,10 @@ timing starts.  Before every timed call the L2s and the Infinity Cache are
 flushed by writing a 1 GiB buffer; each call is timed with HIP events on the
 stream it is launched on.
 
+After the timed loops it measures what this GPU sustains (a plain 4 GiB HBM
+read and an MFMA loop, pod_attn_peak_read / pod_attn_peak_mfma) and reports
+the roofline fraction at those peaks beside the one at the published peaks.
+
 Prints one JSON line (see the keys below).  --gpus N with N > 1 is refused:
 this path runs on one GPU.
 """
