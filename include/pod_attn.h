@@ -230,12 +230,17 @@ typedef struct {
     int32_t persistent;         /* 1 if the fused launch ran as a resident grid       */
     int32_t fixed_order;        /* fused launch: 0 roles claimed after dispatch; 1 / 2
                                    the prefill / decode tasks went to the first
-                                   workgroup ids (a launch resident in one round)     */
+                                   workgroup ids (a launch resident in one round, or
+                                   decode first over several rounds)                 */
     int32_t prefill_priority;   /* 1: prefill waves issued above co-resident decode
                                    waves; 0: equal (a decode-first launch whose
                                    workgroups all start in the first round)         */
     int32_t decode_tail_split_tokens; /* tokens per tail split of a decode request;
                                    0 when the tail is one split                      */
+    int32_t decode_unit_classes;/* 8: the requests' shorter remainder splits run
+                                   longest first in eight length classes (decode-only
+                                   launches and decode-first fused launches of several
+                                   rounds); 1: request order; 0 without decodes      */
 } pod_attn_stats;
 
 /* Validate `cfg`, pick the device, reserve the workspace.  Returns POD_OK and

@@ -103,6 +103,7 @@ void fill_stats(const pod::Plan& pl, pod_attn_stats* st) {
   st->decode_tail_split_tokens = pl.has_d && pl.tail_k ? pl.T2 : 0;
   st->decode_wave_tasks = pl.has_d ? pl.d_wave_tasks : 0;
   st->decode_wg_tasks = pl.has_d ? pl.d_wg_tasks : 0;
+  st->decode_unit_classes = pl.has_d ? pl.rem_buckets : 0;
   st->share_num = pl.share_num;
   st->share_den = pl.share_den;
   st->cu_prefill_x256 = pl.cu_prefill_x256;

@@ -2154,12 +2154,15 @@ DEV void fused_body(const PodParams& p, RunP&& run_prefill, RunD&& run_decode) {
   }
 }
 
-template <class E, int D, int G>
+// RB: remainder phases of the decode unit numbering (1: request order;
+// kRemBuckets: longest first in length classes, for decode-first launches of
+// several rounds, as in decode-only launches).
+template <class E, int D, int G, int RB = 1>
 __global__ __launch_bounds__(256, 2) void pod_hybrid_kernel(PodParams p) {
   POD_DECLARE_LDS(E, D);
   fused_body(
       p, [&](int task) { PfSel<E, D>::run(p, task, lb); },
-      [&](int task) { decode_wg<E, D, G, fused_pf<E, G>()>(p, task, lb); });
+      [&](int task) { decode_wg<E, D, G, fused_pf<E, G>(), RB>(p, task, lb); });
 }
 
 // The three launches of the four-workgroups-per-CU envelope (bf16 only).
@@ -2238,9 +2241,15 @@ template <class E, int D, int G>
 static int launch_t(int which, const PodParams& p, const Plan& pl, hipStream_t s) {
   const dim3 block(256);
   // the decode units were numbered for the kernel family that runs them:
-  // request-order remainders in fused launches, length classes in
-  // decode-only ones (the kernels fix the class count at compile time)
-  if (pl.has_d && pl.rem_buckets != (which == kKernelDecode ? kRemBuckets : 1)) return (int)hipErrorInvalidValue;
+  // length classes in decode-only launches and in decode-first fused
+  // launches of several rounds in the two-workgroup grid, request order in
+  // other fused ones (the kernels fix the class count at compile time)
+  if (pl.has_d) {
+    const bool classes = pl.rem_buckets == kRemBuckets;
+    if (!classes && pl.rem_buckets != 1) return (int)hipErrorInvalidValue;
+    if (which == kKernelDecode && !classes) return (int)hipErrorInvalidValue;
+    if (which == kKernelHybrid && classes && (pl.wg_per_cu != 2 || pl.persistent)) return (int)hipErrorInvalidValue;
+  }
   if (pl.wg_per_cu == 4) {
     if constexpr (E::bytes == 2) {
       switch (which) {
@@ -2262,6 +2271,8 @@ static int launch_t(int which, const PodParams& p, const Plan& pl, hipStream_t s
     case kKernelHybrid:
       if (pl.persistent)
         hipLaunchKernelGGL((pod_persistent_kernel<E, D, G>), dim3(pl.grid), block, 0, s, p);
+      else if (pl.has_d && pl.rem_buckets == kRemBuckets)
+        hipLaunchKernelGGL((pod_hybrid_kernel<E, D, G, kRemBuckets>), dim3(pl.grid), block, 0, s, p);
       else
         hipLaunchKernelGGL((pod_hybrid_kernel<E, D, G>), dim3(pl.grid), block, 0, s, p);
       break;

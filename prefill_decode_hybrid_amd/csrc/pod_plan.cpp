@@ -331,19 +331,30 @@ static int plan_wg(const Shape& s, const Limits& lim, int wg, int mode, const Pr
     // splits (k = 1) or the remainders.  A decode-only launch takes the
     // remainders longest first in eight length classes, which shortened its
     // end on 256 log-uniform contexts (decode alone 1088-1094 -> 1050-1059
-    // us); a fused launch keeps request order, where the prefill fills the
-    // decode's end and the length classes cost 1-3% in the lookup.  The
-    // order never changes a result: a split's record index does not depend
-    // on it.
-    pl.rem_buckets = (pl.has_d && !pl.has_p) ? kRemBuckets : 1;
-    const int np = unit_phases(pl.tail_k, pl.rem_buckets);
+    // us), and so does a decode-first fused launch of several rounds, whose
+    // decode runs the same way (workgroup-id order, below) with the short
+    // prefill in its tail.  Other fused launches keep request order: there
+    // the prefill fills the decode's end and the length classes cost 1-3%
+    // in the lookup.  The order never changes a result (a split's record
+    // index does not depend on it), nor the number of units.
     int64_t per_phase[kUnitPhases] = {};
-    for (int r = 0; r < d.N; ++r)
-      for (int ph = 0; ph < np; ++ph)
-        per_phase[ph] += unit_count(d.ctx_host[r], pl.T, pl.T2, pl.tail_k, ph, pl.rem_buckets);
-    int64_t units = 0;
-    for (int ph = 0; ph < np; ++ph) units += per_phase[ph];
+    auto count_units = [&](int nb) {
+      const int np_nb = unit_phases(pl.tail_k, nb);
+      int64_t n = 0;
+      for (int ph = 0; ph < kUnitPhases; ++ph) per_phase[ph] = 0;
+      for (int r = 0; r < d.N; ++r)
+        for (int ph = 0; ph < np_nb; ++ph)
+          per_phase[ph] += unit_count(d.ctx_host[r], pl.T, pl.T2, pl.tail_k, ph, nb);
+      for (int ph = 0; ph < np_nb; ++ph) n += per_phase[ph];
+      return n;
+    };
+    const int64_t units = count_units(1);
     if (units > (1LL << 30)) return POD_ERR_WORKSPACE;
+    const bool decode_first_rounds = pl.has_p && wg == 2 && !lim.persistent && lim.policy == kPolicyCuBalanced &&
+                                     pl.cu_prefill_x256 == 0 && ceil_div(units * s.hkv, kWavesPerWG) > slots;
+    pl.rem_buckets = (!pl.has_p || decode_first_rounds) ? kRemBuckets : 1;
+    if (pl.rem_buckets != 1) count_units(pl.rem_buckets);
+    const int np = unit_phases(pl.tail_k, pl.rem_buckets);
     int64_t acc = 0;
     for (int ph = 0; ph < np; ++ph) {
       pl.phase_start[ph] = (int)acc;
@@ -361,13 +372,22 @@ static int plan_wg(const Shape& s, const Limits& lim, int wg, int mode, const Pr
   // schedule without the claims' atomics in front of the work: decode first
   // with every decode workgroup resident at once, or a launch whose whole
   // grid is resident at once (prefill first: the dispatcher spreads the
-  // first workgroup ids over the CUs).  Launches of several rounds keep the
-  // claims, which balance the CUs and XCDs as workgroups come and go.
+  // first workgroup ids over the CUs).  A decode-first launch of several
+  // rounds also hands the decode tasks to the first ids, in the decode-only
+  // launch's length-class order, and the prefill's to the last: on 256
+  // log-uniform decodes beside a 256-row chunk, 1082 us against 1102-1123
+  // with claims in request order and 1096 for the split launches back to
+  // back (by id in request order it measured 1117, prefill first by id 1097
+  // with the classes and 1133 without).  Other launches of several rounds
+  // keep the claims, which balance the CUs and XCDs as workgroups come and
+  // go.
   if (pl.has_p && pl.has_d && !lim.persistent && lim.policy == kPolicyCuBalanced) {
     if (pl.cu_prefill_x256 == 0 && pl.d_wg_tasks <= slots)
       pl.fixed_order = 2;
     else if (pl.grid <= slots)
       pl.fixed_order = 1;
+    else if (pl.cu_prefill_x256 == 0 && pl.rem_buckets != 1)
+      pl.fixed_order = 2;
   }
   // Prefill waves issue above co-resident decode waves where the prefill is
   // the longer role or runs in the decode's tail.  When a decode-first

@@ -121,7 +121,7 @@ struct Plan {
   int d_median = 0;     // median decode context
   int64_t d_total = 0;  // sum of decode contexts
   int T2 = 0, tail_k = 0;  // short (tail) split length, long splits moved to the tail (pod_units.h)
-  int rem_buckets = 1;  // remainder phases of the unit numbering (kRemBuckets only for decode-only launches)
+  int rem_buckets = 1;  // remainder phases of the unit numbering (kRemBuckets: decode-only and decode-first multi-round fused launches)
   int phase_start[kUnitPhases + 1] = {};  // first decode unit of every phase (pod_units.h)
   // fused scheduling
   int share_num = 0, share_den = 1, cu_prefill_x256 = 0, policy = 0;

@@ -174,12 +174,14 @@ def test_role_mix_by_work_ratio(P0, x):
     assert st["decode_wg_tasks"] <= 256 * st["wg_per_cu"]
 
 
-def test_fixed_order_only_for_one_round():
-    # the decode-heavy batch runs decode first over several rounds: claims stay
+def test_fixed_order_rule():
+    # the decode-heavy batch runs decode first over several rounds: decode
+    # tasks to the first workgroup ids, in length classes (as decode alone)
     spec = inputs.CONFIGS[4]
     st = plan(_cfg(4), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
               _decode(inputs.draw_context_lens(4, 0)))
-    assert st["cu_prefill_x256"] == 0 and st["decode_wg_tasks"] > 512 and st["fixed_order"] == 0
+    assert st["cu_prefill_x256"] == 0 and st["decode_wg_tasks"] > 512 and st["fixed_order"] == 2
+    assert st["decode_unit_classes"] == 8 and st["prefill_priority"] == 1
     for kw in (dict(persistent=1), dict(policy=pod.POD_POLICY_PROPORTIONAL)):
         st = plan(_cfg(3, **kw), pod.MODE_HYBRID, _prefill(512, 0), _decode([16384] * 64))
         assert st["fixed_order"] == 0
@@ -200,6 +202,34 @@ def test_fixed_order_only_for_one_round():
     st = plan(_cfg(3), pod.MODE_HYBRID, _prefill(spec["chunk_len"], spec["chunk_offset"]),
               _decode(inputs.draw_context_lens(3, 0)))
     assert st["grid"] > 512 and st["fixed_order"] == 0
+
+
+def test_decode_unit_classes_rule():
+    # length classes (remainders longest first) where the decode's end is not
+    # filled by a prefill: decode-only calls and decode-first fused launches
+    # of several rounds; request order in other fused launches
+    spec4 = inputs.CONFIGS[4]
+    ctx4 = inputs.draw_context_lens(4, 0)
+    pa4 = _prefill(spec4["chunk_len"], spec4["chunk_offset"])
+    assert plan(_cfg(4), pod.MODE_DECODE, None, _decode(ctx4))["decode_unit_classes"] == 8
+    # the same batch with the role order or the grid changed: request order, claims
+    for kw in (dict(persistent=1), dict(policy=pod.POD_POLICY_PROPORTIONAL), dict(prefill_slots_x256=256),
+               dict(wg_per_cu=4)):
+        st = plan(_cfg(4, **kw), pod.MODE_HYBRID, pa4, _decode(ctx4))
+        assert st["decode_unit_classes"] == 1 and st["fixed_order"] == 0, kw
+    # decode first in one round (Llama batch) and the overlapped long-context batch: request order
+    spec2 = inputs.CONFIGS[2]
+    st = plan(_cfg(2), pod.MODE_HYBRID, _prefill(spec2["chunk_len"], spec2["chunk_offset"]),
+              _decode(inputs.draw_context_lens(2, 0)))
+    assert st["cu_prefill_x256"] == 0 and st["decode_unit_classes"] == 1
+    spec3 = inputs.CONFIGS[3]
+    st = plan(_cfg(3), pod.MODE_HYBRID, _prefill(spec3["chunk_len"], spec3["chunk_offset"]),
+              _decode(inputs.draw_context_lens(3, 0)))
+    assert st["cu_prefill_x256"] > 0 and st["decode_unit_classes"] == 1
+    # the units are the same set in every numbering
+    assert (plan(_cfg(4), pod.MODE_HYBRID, pa4, _decode(ctx4))["decode_wave_tasks"]
+            == plan(_cfg(4, persistent=1), pod.MODE_HYBRID, pa4, _decode(ctx4))["decode_wave_tasks"])
+    assert plan(_cfg(4), pod.MODE_PREFILL, _prefill(256, 0), None)["decode_unit_classes"] == 0
 
 
 def test_prefill_priority_rule():
