@@ -86,7 +86,9 @@ enum pod_dtype { POD_BF16 = 0, POD_F32 = 1 };
  * proportional and 50:50 ticket sequences (§5.4.2) and a fixed split by
  * workgroup id, i.e. CTA-parallel fusion without SM awareness (§3.3). */
 enum pod_policy {
-    POD_POLICY_CU_BALANCED = 0,  /* per-CU running counts; prefill slots from the batch  */
+    POD_POLICY_CU_BALANCED = 0,  /* per-CU running counts; prefill slots from the batch
+                                    (a prefill-first launch of several rounds takes the
+                                    proportional rule instead; the stats report it)     */
     POD_POLICY_PROPORTIONAL = 1, /* per-CU tickets, prefill share = prefill / all tasks */
     POD_POLICY_HALF = 2,         /* per-CU tickets alternating prefill and decode       */
     POD_POLICY_STATIC = 3        /* workgroup id decides the role, no CU awareness      */

@@ -182,7 +182,11 @@ def main(argv=None):
     s = summarize(att.role_trace(), plan["num_cus"], a.buckets, dbytes)
     att.close()
     workload = f"config{a.config}_{b.spec['name']}"
-    out = {"workload": workload, "wg_per_cu": plan["wg_per_cu"], "policy": a.policy,
+    # the role rule the launch ran (the planner may take another rule than the
+    # configured CU-balanced one; the stats report it)
+    pol = plan["policy"]
+    pol_text = f"policy {pol}" + (f" (configured {a.policy})" if pol != a.policy else "")
+    out = {"workload": workload, "wg_per_cu": plan["wg_per_cu"], "policy": pol, "configured_policy": a.policy,
            "planned_prefill_slots_per_cu": plan["cu_prefill_x256"] / 256, "fixed_order": plan["fixed_order"],
            "grid": plan["grid"], "summary": s}
     print(json.dumps(out), flush=True)
@@ -192,7 +196,7 @@ def main(argv=None):
         lines = [f"# Realised role mix: {workload}", "", "Command:", "", "```", cmd, "```", "",
                  f"Plan: {plan['wg_per_cu']} workgroups per CU, {plan['grid']} workgroups, "
                  f"{plan['prefill_tasks']} prefill tasks, {plan['decode_wg_tasks']} decode workgroup tasks, "
-                 f"planned prefill slots per CU {plan['cu_prefill_x256'] / 256:.3f}, policy {a.policy}, "
+                 f"planned prefill slots per CU {plan['cu_prefill_x256'] / 256:.3f}, {pol_text}, "
                  f"roles {'by workgroup id' if plan['fixed_order'] else 'claimed after dispatch'}.", "",
                  "| quantity | value |", "|---|---|"]
         for k, v in s.items():

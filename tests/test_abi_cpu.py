@@ -204,6 +204,26 @@ def test_fixed_order_rule():
     assert st["grid"] > 512 and st["fixed_order"] == 0
 
 
+def test_prefill_first_rounds_take_proportional_tickets():
+    # the prefill-heavy batch: prefill takes every slot over several rounds,
+    # so the CU-balanced policy hands the roles out by proportional tickets
+    spec = inputs.CONFIGS[5]
+    pa, da = _prefill(spec["chunk_len"], spec["chunk_offset"]), _decode(inputs.draw_context_lens(5, 0))
+    st = plan(_cfg(5), pod.MODE_HYBRID, pa, da)
+    assert st["cu_prefill_x256"] == 512 and st["grid"] > 512 and st["policy"] == pod.POD_POLICY_PROPORTIONAL
+    assert st["share_num"] * (st["prefill_tasks"] + st["decode_wg_tasks"]) == pytest.approx(
+        st["share_den"] * st["prefill_tasks"], rel=0.02)
+    # not where the config fixes another policy or the grid, nor for the other batches
+    assert plan(_cfg(5, policy=pod.POD_POLICY_HALF), pod.MODE_HYBRID, pa, da)["policy"] == pod.POD_POLICY_HALF
+    assert plan(_cfg(5, persistent=1), pod.MODE_HYBRID, pa, da)["policy"] == pod.POD_POLICY_CU_BALANCED
+    assert plan(_cfg(5, prefill_slots_x256=448), pod.MODE_HYBRID, pa, da)["policy"] == pod.POD_POLICY_CU_BALANCED
+    for cid in (2, 3, 4):
+        sp = inputs.CONFIGS[cid]
+        st = plan(_cfg(cid), pod.MODE_HYBRID, _prefill(sp["chunk_len"], sp["chunk_offset"]),
+                  _decode(inputs.draw_context_lens(cid, 0)))
+        assert st["policy"] == pod.POD_POLICY_CU_BALANCED, cid
+
+
 def test_decode_unit_classes_rule():
     # length classes (remainders longest first) where the decode's end is not
     # filled by a prefill: decode-only calls and decode-first fused launches
