@@ -373,8 +373,9 @@ static int plan_wg(const Shape& s, const Limits& lim, int wg, int mode, const Pr
   // decode workgroups then run spread over the launch beside prefill tiles
   // instead of after them, where the last prefill round's ragged end left
   // most slots idle (prefill-heavy batch, side by side in one process:
-  // 2320-2324 -> 2273 us; 1-2% on two earlier boxes).
-  if (pl.has_p && pl.has_d && !lim.persistent && lim.policy == kPolicyCuBalanced &&
+  // 2320-2324 -> 2273 us; 1-2% on two earlier boxes).  Prefill slots fixed
+  // in the config keep the CU-balanced rule they ask for.
+  if (pl.has_p && pl.has_d && !lim.persistent && lim.policy == kPolicyCuBalanced && lim.slots_x256 == 0 &&
       pl.cu_prefill_x256 == 256 * wg && pl.grid > slots)
     pl.policy = kPolicyProportional;
   // Roles by workgroup id instead of claims, when that runs the same

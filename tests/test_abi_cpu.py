@@ -216,7 +216,9 @@ def test_prefill_first_rounds_take_proportional_tickets():
     # not where the config fixes another policy or the grid, nor for the other batches
     assert plan(_cfg(5, policy=pod.POD_POLICY_HALF), pod.MODE_HYBRID, pa, da)["policy"] == pod.POD_POLICY_HALF
     assert plan(_cfg(5, persistent=1), pod.MODE_HYBRID, pa, da)["policy"] == pod.POD_POLICY_CU_BALANCED
-    assert plan(_cfg(5, prefill_slots_x256=448), pod.MODE_HYBRID, pa, da)["policy"] == pod.POD_POLICY_CU_BALANCED
+    for slots in (448, 512):
+        st = plan(_cfg(5, prefill_slots_x256=slots), pod.MODE_HYBRID, pa, da)
+        assert st["policy"] == pod.POD_POLICY_CU_BALANCED and st["cu_prefill_x256"] == slots
     for cid in (2, 3, 4):
         sp = inputs.CONFIGS[cid]
         st = plan(_cfg(cid), pod.MODE_HYBRID, _prefill(sp["chunk_len"], sp["chunk_offset"]),
