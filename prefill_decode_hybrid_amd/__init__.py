@@ -287,9 +287,19 @@ def pod_attn_plan_varlen(cfg: PodAttnConfig, num_cus: int, mode: int, prefill=No
     return st.as_dict()
 
 
+def _check_device_bytes(t, nbytes: int, what: str) -> None:
+    """A tensor argument must hold at least nbytes of device memory (a raw
+    pointer is the caller's responsibility)."""
+    if hasattr(t, "data_ptr"):
+        if not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{what}: needs a contiguous device tensor of at least {nbytes} bytes")
+
+
 def pod_attn_peak_read(buf, nbytes: int, workgroups: int, sink, stream=None) -> None:
     """Enqueue the HBM-read kernel over `nbytes` of device buffer `buf` (a
     tensor or pointer); `sink` is a device uint32 word (tensor or pointer)."""
+    _check_device_bytes(buf, int(nbytes), "pod_attn_peak_read buffer")
+    _check_device_bytes(sink, 4, "pod_attn_peak_read sink")
     rc = load().pod_attn_peak_read(_ptr(buf) if hasattr(buf, "data_ptr") else buf, int(nbytes), int(workgroups),
                                    _ptr(sink) if hasattr(sink, "data_ptr") else sink, _stream_ptr(stream))
     if rc != POD_OK:
@@ -298,6 +308,7 @@ def pod_attn_peak_read(buf, nbytes: int, workgroups: int, sink, stream=None) -> 
 
 def pod_attn_peak_mfma(workgroups: int, iters: int, sink, stream=None) -> None:
     """Enqueue the MFMA loop: workgroups x 4 waves x iters x 16 bf16 32x32x16 MFMAs."""
+    _check_device_bytes(sink, 4, "pod_attn_peak_mfma sink")
     rc = load().pod_attn_peak_mfma(int(workgroups), int(iters), _ptr(sink) if hasattr(sink, "data_ptr") else sink,
                                    _stream_ptr(stream))
     if rc != POD_OK:

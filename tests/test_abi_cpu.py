@@ -525,3 +525,13 @@ def test_peak_kernels_validate_before_launch(lib):
     assert lib.pod_attn_peak_mfma(0, 8, FAKE, None) == inv
     assert lib.pod_attn_peak_mfma(4, 0, FAKE, None) == inv
     assert lib.pod_attn_peak_mfma(4, 8, None, None) == inv
+
+
+def test_peak_wrappers_check_tensor_sizes():
+    # a host or undersized tensor never reaches the kernel
+    import torch
+    small = torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        pod.pod_attn_peak_read(small, 1 << 20, 4, torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        pod.pod_attn_peak_mfma(4, 8, torch.zeros(1, dtype=torch.int32))
